@@ -1,0 +1,26 @@
+"""CPU oracle for the W8A8 int8-dynamic linear layer.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The product path (the HIP library
+and its Python binding) never calls it, and the two share no code; both take
+their inputs from the seeded generators in ``synth_inputs``.
+
+Every function follows a passage of the pages; see ``oracle.w8a8_oracle``.
+"""
+from .w8a8_oracle import (  # noqa: F401
+    K_MAX,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    quant_rows,
+    quant_act,
+    quantize_weights,
+    gemm_exact,
+    gemm_int64_rows,
+    epilogue_f32,
+    epilogue,
+    linear,
+    dequant_reference,
+    float_reference,
+    noise_model_rel_l2,
+    rel_l2,
+)

@@ -1,0 +1,243 @@
+"""Plain, slow CPU oracle of the W8A8 int8-dynamic linear layer.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+What is computed (y = W8A8 linear of bf16 activations x [M,K] and bf16
+weights W [N,K]):
+
+  1. per-token (per-row) symmetric int8 quantisation of x with
+     scale = amax/127,
+  2. per-output-channel symmetric int8 quantisation of W with an fp32 scale
+     per output channel,
+  3. an int8 x int8 product with exact integer accumulation, stored as int32,
+  4. an fp32 epilogue acc * act_scale * weight_scale (+ bias) rounded to bf16.
+
+Sources (page titles and sections; the pages are the authority):
+
+* "Issue 5 probe: int8 quantized DiT serve paths on the RTX 3090 (24 GB)",
+  section "Round two ... W8A8 int8-dynamic": int8 weights with dynamic
+  per-token symmetric int8 activations, served by an int8 scaled-MM; the
+  artifact stores unpacked int8 weights with fp32 per-channel scales; the
+  probe's reference has to carry the act_scale factor (the 97% error scare
+  was that factor missing). Section "Kernel isolation": the reference the
+  layer is compared against is float32 x @ dequant(W)^T.
+* "Int8 Quantization" (vLLM-Omni user guide), sections "Overview" and
+  "Parameters": BF16/FP16 weights are quantised at load time; only dynamic
+  (online) activation scaling exists.
+* "Qwen-Image-2.1: TE AutoRound-AWQ on GPU + all-resident single-3090 stack",
+  section "Whole-pipeline follow-up": per-token activation and per-channel
+  weight quantisation.
+* unsloth commit log of test_diffusion_transformer_quant.py: int8 matmuls run
+  with int32 accumulation.
+
+Readings where the pages are silent (each is a choice this oracle fixes and
+the HIP path must reproduce):
+
+* scale = fl32(amax / 127) by one IEEE fp32 division; q = fl32(x / scale)
+  by a second IEEE fp32 division, then round half to even, then clamp to
+  [-127, 127] ("symmetric": -128 is never produced).
+* all-zero row: scale = 0 and q = 0.
+* both scales are fp32.
+* epilogue order ((fl32(acc) * s_a) * s_w) + fp32(bias), each step rounded
+  to fp32 (no fused multiply-add), then bf16 round to nearest even.
+* bias is optional and added after both scales.
+* the integer product is exact; |acc| <= 127^2 K must fit int32, so
+  K <= 133 144.
+* subnormal inputs are legal and are not flushed; NaN/Inf inputs are outside
+  the contract.
+
+Parity pins: every function here is checked by tests that do not call it
+back (hand-computed golden files, exact rational arithmetic, brute force,
+closed forms, invariants, a library cast, and the pages' 0.17% figure).
+No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# |acc| <= 127 * 127 * K must fit in int32.
+K_MAX = (2**31 - 1) // (127 * 127)          # 133 144
+
+_F32_127 = np.float32(127.0)
+
+
+# --- bf16 <-> fp32 -------------------------------------------------------
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact: bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_bf16_bits(t) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    Adding 0x7FFF plus the lowest kept bit and dropping the low 16 bits is
+    RNE on the magnitude; overflow past the largest finite value carries into
+    the exponent and gives infinity, as IEEE rounding does. NaN stays NaN.
+    """
+    f = np.asarray(t, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(f)
+    if np.any(nan):
+        r = np.where(nan, ((u >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16), r)
+    return r
+
+
+# --- step 1/2: symmetric per-row int8 quantisation -----------------------
+
+def quant_rows(rows_f32) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row symmetric int8 quantisation: returns (q int8 [R,K], scale fp32 [R]).
+
+    Issue 5 probe, "Round two": dynamic per-token symmetric int8 activations;
+    the same per-row maths gives the per-output-channel weight quantisation
+    with fp32 scales (same section, artifact description).
+    """
+    a = np.asarray(rows_f32, dtype=np.float32)
+    if a.ndim != 2:
+        raise ValueError("rows must be 2-D")
+    R, K = a.shape
+    q = np.zeros((R, K), dtype=np.int8)
+    if K == 0:
+        return q, np.zeros(R, dtype=np.float32)
+    amax = np.max(np.abs(a), axis=1)                      # exact
+    scale = (amax / _F32_127).astype(np.float32)          # one fp32 division
+    nz = scale != 0
+    if np.any(nz):
+        quot = a[nz] / scale[nz][:, None]                 # fp32 division
+        assert quot.dtype == np.float32
+        q[nz] = np.clip(np.rint(quot), -127, 127).astype(np.int8)  # RNE
+    return q, scale
+
+
+def quant_act(x_bits) -> tuple[np.ndarray, np.ndarray]:
+    """Dynamic per-token quantisation of bf16 activations [M,K]."""
+    return quant_rows(bf16_bits_to_f32(x_bits))
+
+
+def quantize_weights(w_bits) -> tuple[np.ndarray, np.ndarray]:
+    """Load-time per-output-channel quantisation of bf16 weights [N,K]
+    (Int8 Quantization guide, "Overview": quantise BF16/FP16 weights at load).
+    """
+    return quant_rows(bf16_bits_to_f32(w_bits))
+
+
+# --- step 3: int8 x int8 -> int32 ----------------------------------------
+
+def _check_k(K: int) -> None:
+    if K > K_MAX:
+        raise ValueError(f"K={K} exceeds {K_MAX}: int32 accumulation could overflow")
+
+
+def gemm_exact(q, wq) -> np.ndarray:
+    """acc[m,n] = sum_k q[m,k] * wq[n,k], exact, as int32.
+
+    Computed with float64 BLAS on the int8-valued operands: every product and
+    every partial sum is an integer of magnitude <= 127^2 K < 2^53, so any
+    summation order gives the exact sum.
+    """
+    q = np.asarray(q, dtype=np.int8)
+    wq = np.asarray(wq, dtype=np.int8)
+    if q.shape[1] != wq.shape[1]:
+        raise ValueError("K mismatch")
+    _check_k(q.shape[1])
+    acc = q.astype(np.float64) @ wq.astype(np.float64).T
+    return acc.astype(np.int64).astype(np.int32)
+
+
+def gemm_int64_rows(q, wq, rows=None) -> np.ndarray:
+    """The same sum with literal int64 integer arithmetic, for chosen rows."""
+    q = np.asarray(q, dtype=np.int8)
+    wq64 = np.asarray(wq, dtype=np.int8).astype(np.int64)
+    _check_k(q.shape[1])
+    idx = range(q.shape[0]) if rows is None else rows
+    out = [wq64 @ q[m].astype(np.int64) for m in idx]
+    if not out:
+        return np.zeros((0, wq64.shape[0]), dtype=np.int64)
+    return np.stack(out)
+
+
+# --- step 4: epilogue ----------------------------------------------------
+
+def epilogue_f32(acc, s_a, s_w, bias_bits=None) -> np.ndarray:
+    """fp32 value before the bf16 cast: ((fl32(acc) * s_a) * s_w) + bias.
+
+    Issue 5 probe, "Round two": the result must carry act_scale (and the
+    per-channel weight scale). Each operation rounds to fp32 separately.
+    """
+    t = np.asarray(acc, dtype=np.int32).astype(np.float32)   # RNE beyond 2^24
+    t = t * np.asarray(s_a, dtype=np.float32)[:, None]
+    t = t * np.asarray(s_w, dtype=np.float32)[None, :]
+    if bias_bits is not None:
+        t = t + bf16_bits_to_f32(bias_bits)[None, :]
+    assert t.dtype == np.float32
+    return t
+
+
+def epilogue(acc, s_a, s_w, bias_bits=None) -> np.ndarray:
+    """bf16 output bits of the epilogue."""
+    return f32_to_bf16_bits(epilogue_f32(acc, s_a, s_w, bias_bits))
+
+
+# --- whole layer ---------------------------------------------------------
+
+def linear(x_bits, wq, s_w, bias_bits=None) -> dict:
+    """W8A8 linear of bf16 x [M,K] with prepared int8 weights [N,K], fp32 s_w.
+
+    Returns xq, s_a, acc (int32) and y (bf16 bits) so every intermediate can
+    be compared.
+    """
+    xq, s_a = quant_act(x_bits)
+    acc = gemm_exact(xq, wq)
+    y = epilogue(acc, s_a, s_w, bias_bits)
+    return {"xq": xq, "s_a": s_a, "acc": acc, "y": y}
+
+
+# --- references the pages compare against -------------------------------
+
+def dequant_reference(xq, s_a, wq, s_w, bias_bits=None) -> np.ndarray:
+    """float64 (xq * s_a) @ (wq * s_w)^T (+ bias): the layer on its own
+    quantised operands, which is what the Issue 5 probe compared the int8 ops
+    against ("Kernel isolation": float32 x @ dequant(W)^T, with act_scale).
+    """
+    a = np.asarray(xq, np.float64) * np.asarray(s_a, np.float64)[:, None]
+    b = np.asarray(wq, np.float64) * np.asarray(s_w, np.float64)[:, None]
+    r = a @ b.T
+    if bias_bits is not None:
+        r = r + bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return r
+
+
+def float_reference(x_bits, w_bits, bias_bits=None) -> np.ndarray:
+    """Unquantised float64 x @ W^T (+ bias)."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    r = x @ w.T
+    if bias_bits is not None:
+        r = r + bf16_bits_to_f32(bias_bits).astype(np.float64)[None, :]
+    return r
+
+
+def noise_model_rel_l2(x_bits, w_bits, xq, s_a, wq, s_w) -> float:
+    """Predicted rel-L2 of the quantised layer against the unquantised one.
+
+    With independent, zero-mean rounding errors e_x (activations) and e_w
+    (weights), E||(x+e_x)(W+e_w)^T - xW^T||^2 ~= sum e_x^2 (W^2)^T +
+    sum x^2 (e_w^2)^T (the e_x e_w term is second order).
+    """
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    w = bf16_bits_to_f32(w_bits).astype(np.float64)
+    ex = np.asarray(xq, np.float64) * np.asarray(s_a, np.float64)[:, None] - x
+    ew = np.asarray(wq, np.float64) * np.asarray(s_w, np.float64)[:, None] - w
+    var = (ex**2 @ (w**2).T).sum() + (x**2 @ (ew**2).T).sum()
+    ref = x @ w.T
+    return float(np.sqrt(var) / np.linalg.norm(ref))
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))

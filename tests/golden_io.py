@@ -1,0 +1,49 @@
+"""Readers for the hand-computed fixtures under tests/golden/."""
+from __future__ import annotations
+
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+def _num(tok: str) -> float:
+    if "0x" in tok and "p" in tok:
+        return float.fromhex(tok)
+    return float(tok)
+
+
+def _lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for raw in f:
+            line = raw.strip()
+            if line and not line.startswith("#"):
+                yield line
+
+
+def quant_cases():
+    """[(x values, scale, q values)]"""
+    out = []
+    for line in _lines("quant_hand_cases.txt"):
+        xs, s, qs = (p.strip() for p in line.split("|"))
+        out.append(([_num(t) for t in xs.split()], _num(s), [int(t) for t in qs.split()]))
+    return out
+
+
+def epilogue_cases():
+    """[(acc, s_a, s_w, bias_bits or None, y_bits)]"""
+    out = []
+    for line in _lines("epilogue_hand_cases.txt"):
+        lhs, y = (p.strip() for p in line.split("|"))
+        acc, sa, sw, b = lhs.split()
+        bias = None if b == "-" else int(b, 16)
+        out.append((int(acc), _num(sa), _num(sw), bias, int(y, 16)))
+    return out
+
+
+def gemm_case():
+    rows = {"xq": [], "wq": [], "acc": []}
+    for line in _lines("gemm_hand_case.txt"):
+        tag, *vals = line.split()
+        rows[tag].append([int(v) for v in vals])
+    return rows["xq"], rows["wq"], rows["acc"]
