@@ -1,0 +1,264 @@
+"""Benchmark of the W8A8 int8-dynamic linear on one MI355X.
+
+One step = one pass of the whole hot path over one 1024px diffusion
+transformer block: the four block linears at M = 4352 tokens (fused QKV
+3072->9216, out-proj 3072->3072, FFN up 3072->12288, FFN down 12288->3072),
+each as dynamic activation quantisation + int8 MFMA GEMM with the fused
+scale epilogue, plus the AdaLN modulation projection 3072->18432 at M = 1 on
+the fused small-M kernel. Weights are quantised once before timing (load
+time); inputs are synthetic (seeded, see synth_inputs) and resident in HBM.
+
+Prints one JSON line. `value` is int8 TOPS of the whole step; per-shape
+figures, the roofline of the dominant kernel (the GEMM, bound by int8 MFMA
+throughput) and the CPU oracle's rate on the same step ride along.
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("int8 TOPS + % of MI355X int8 MFMA peak (HBM GB/s for M≤16), per shape")
+PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+GEMM_KERNEL = "gemm_i8_kernel"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_i8_dit_block_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip timing the CPU oracle (profiling runs)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "w8a8_int8_dynamic_quant_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(gemm_launch_ops):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    or None when the kernels changed since the counters were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch_avg")
+
+
+def cpu_baseline(inputs, wq_host):
+    """The oracle, as it stands, on one whole step (all five linears)."""
+    import numpy as np
+
+    import oracle
+    ops = 0
+    t0 = time.perf_counter()
+    for name, d in inputs.items():
+        wq, sw = wq_host[name]
+        oracle.linear(d["x"], wq, sw, d["bias"])
+        ops += 2 * d["M"] * d["N"] * d["K"]
+    dt = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {
+        "value": ops / dt / 1e12,
+        "unit": "TOPS",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": "one whole step: the 4 DiT block linears at M=4352 and the M=1 "
+                  "modulation projection (quantise, exact int GEMM, fp32 epilogue)",
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": platform.processor() or platform.machine(),
+        "numpy": np.__version__,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the path shards by rows or columns with no communication; "
+              "multi-GPU timing is out of scope)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import w8a8_int8_dynamic_quant_amd as w8
+    from synth_inputs import DIT_BLOCK, SPECS, make_linear_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w8.lib()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    inputs = {name: make_linear_inputs(name) for name in DIT_BLOCK}
+    layers = []
+    for name in DIT_BLOCK:
+        d = inputs[name]
+        M, K, N = d["M"], d["K"], d["N"]
+        wq, sw = w8.quantize_weights(to_dev(d["w"]))            # load time, untimed
+        layers.append({
+            "name": name, "M": M, "K": K, "N": N,
+            "x": to_dev(d["x"]), "wq": wq, "sw": sw,
+            "bias": None if d["bias"] is None else to_dev(d["bias"]),
+            "xq": torch.empty((M, K), dtype=torch.int8, device=dev),
+            "sa": torch.empty((M,), dtype=torch.float32, device=dev),
+            "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+            "ws": torch.empty((w8.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev),
+            "path": w8.linear_path(M, K, N),
+        })
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for i, L in enumerate(layers):
+            if L["path"] == w8.PATH_GEMM:
+                # w8a8_linear on this path launches exactly these two kernels;
+                # calling the two entry points lets events bracket each one.
+                if events is not None:
+                    events[i][0].record(stream)
+                st = w8.lib().w8a8_quant_act(
+                    L["x"].data_ptr(), L["M"], L["K"], L["K"], L["xq"].data_ptr(),
+                    L["sa"].data_ptr(), stream.cuda_stream)
+                if events is not None:
+                    events[i][1].record(stream)
+                st |= w8.lib().w8a8_scaled_mm(
+                    L["xq"].data_ptr(), L["sa"].data_ptr(), L["M"], L["K"], L["wq"].data_ptr(),
+                    L["sw"].data_ptr(), L["N"],
+                    None if L["bias"] is None else L["bias"].data_ptr(),
+                    L["out"].data_ptr(), L["N"], None, stream.cuda_stream)
+                if events is not None:
+                    events[i][2].record(stream)
+            else:
+                if events is not None:
+                    events[i][0].record(stream)
+                    events[i][1].record(stream)
+                st = w8.lib().w8a8_linear(
+                    L["x"].data_ptr(), L["M"], L["K"], L["K"], L["wq"].data_ptr(),
+                    L["sw"].data_ptr(), L["N"],
+                    None if L["bias"] is None else L["bias"].data_ptr(),
+                    L["out"].data_ptr(), L["N"], L["ws"].data_ptr(), L["ws"].numel(), None,
+                    stream.cuda_stream)
+                if events is not None:
+                    events[i][2].record(stream)
+            if st != 0:
+                raise RuntimeError(f"{L['name']}: libw8a8 status {st}")
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers]
+          for _ in range(args.steps)]
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = wall * 1e3 / args.steps
+    ops_step = sum(2 * L["M"] * L["N"] * L["K"] for L in layers)
+    per_shape = []
+    gemm_ops = gemm_ms = 0.0
+    gemm_launches = 0
+    for i, L in enumerate(layers):
+        qs = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        gs = [ev[s][i][1].elapsed_time(ev[s][i][2]) for s in range(args.steps)]
+        q_ms, g_ms = float(np.mean(qs)), float(np.mean(gs))
+        tot = q_ms + g_ms
+        M, K, N = L["M"], L["K"], L["N"]
+        ops = 2 * M * N * K
+        alg_bytes = 2 * M * K + N * K + 4 * N + (2 * N if L["bias"] is not None else 0) + 2 * M * N
+        row = {"shape": L["name"], "M": M, "K": K, "N": N,
+               "path": "gemm" if L["path"] == w8.PATH_GEMM else "small_m",
+               "us": tot * 1e3, "tops": ops / (tot * 1e-3) / 1e12,
+               "pct_int8_peak": 100 * ops / (tot * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+               "gbs": alg_bytes / (tot * 1e-3) / 1e9,
+               "pct_hbm": 100 * alg_bytes / (tot * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               "us_median": float(np.median(np.add(qs, gs))) * 1e3}
+        if L["path"] == w8.PATH_GEMM:
+            row["quant_us"] = q_ms * 1e3
+            row["quant_gbs"] = (3 * M * K + 4 * M) / (q_ms * 1e-3) / 1e9
+            row["gemm_us"] = g_ms * 1e3
+            row["gemm_tops"] = ops / (g_ms * 1e-3) / 1e12
+            row["gemm_tile"] = list(w8.gemm_tile(M, K, N))
+            gemm_ops += ops
+            gemm_ms += g_ms
+            gemm_launches += 1
+        per_shape.append(row)
+
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": GEMM_KERNEL,
+        "achieved": achieved,
+        "peak": PEAK_INT8_TOPS,
+        "unit": "TOPS",
+        "frac": achieved / PEAK_INT8_TOPS,
+        "traffic": load_traffic(gemm_ops / gemm_launches),
+        "avg_launch_us": gemm_ms * 1e3 / gemm_launches,
+        "ops_per_launch_avg": gemm_ops / gemm_launches,
+    }
+
+    line = {
+        "metric": METRIC,
+        "value": ops_step / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "dit_block_1024px_w8a8",
+                   "linears": [f"{L['M']}x{L['K']}x{L['N']}" for L in layers],
+                   "tokens": 4352, "hidden": 3072, "mlp": 12288},
+        "roofline": roofline,
+        "per_shape": per_shape,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        import oracle
+        wq_host = {name: oracle.quantize_weights(inputs[name]["w"]) for name in DIT_BLOCK}
+        line["cpu_baseline"] = cpu_baseline(inputs, wq_host)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * w8a8.h - C ABI of libw8a8, the W8A8 int8-dynamic linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer (sources are the pages' titles and sections):
+ *
+ *   y[m,n] = bf16( ((fl32(acc[m,n]) * a_scale[m]) * w_scale[n]) + bias[n] )
+ *   acc[m,n] = sum_k xq[m,k] * wq[n,k]                 (exact, int32)
+ *   xq, a_scale = per-row symmetric int8 quantisation of x (dynamic)
+ *   wq, w_scale = per-row symmetric int8 quantisation of W (load time)
+ *
+ * - "Issue 5 probe: int8 quantized DiT serve paths on the RTX 3090 (24 GB)",
+ *   section "Round two ... W8A8 int8-dynamic": int8 weights, dynamic
+ *   per-token symmetric int8 activations, an int8 scaled matrix product; the
+ *   stored artifact is unpacked int8 weights plus fp32 per-channel scales;
+ *   the result carries act_scale.
+ * - "Int8 Quantization" (vLLM-Omni user guide), "Overview" and "Parameters":
+ *   weights are quantised at load time or loaded pre-quantised; activation
+ *   scaling is dynamic only.
+ * - unsloth test_diffusion_transformer_quant.py commit log: int8 products
+ *   accumulate in int32; the torch._int_mm route needs M > 16 and so could
+ *   not serve the M = 1 modulation projections. This library has no such
+ *   limit: M <= W8A8_SMALL_M goes to a bandwidth-bound small-M kernel.
+ *
+ * Per-row quantisation of a row r[0..K-1]:
+ *   amax = max_k |r[k]|,  scale = fl32(amax / 127)   (IEEE fp32 division)
+ *   q[k] = clamp(round_half_even(fl32(r[k] / scale)), -127, 127)
+ *   an all-zero row gives scale = 0 and q = 0.
+ *
+ * Conventions for every entry point:
+ * - Pointers are DEVICE pointers owned by the caller. The library allocates
+ *   nothing, keeps no state between calls, is reentrant, never writes its
+ *   inputs, and only enqueues work on `stream` (a hipStream_t passed as
+ *   void*; NULL = the default stream). A call returns once the work is
+ *   enqueued; the caller keeps every buffer alive until the stream has run it.
+ * - Layouts are row-major. bf16 values are passed as uint16_t bit patterns.
+ * - Arguments are validated before anything is launched; on an error nothing
+ *   is enqueued and an error status is returned (no exceptions, no abort).
+ * - Requirements: M >= 0 (M == 0 is a no-op), N >= 1, 16 <= K <= W8A8_K_MAX
+ *   and K % 16 == 0 (else W8A8_ERR_UNSUPPORTED); every leading dimension
+ *   ld >= K (ldo >= N); bf16 input leading dimensions are multiples of 8;
+ *   x/w/xq/wq/workspace pointers 16-byte aligned, scale/bias/out/acc_debug
+ *   pointers 4-byte aligned (else W8A8_ERR_MISALIGNED).
+ * - Outputs are undefined if an output buffer overlaps any other buffer.
+ * - Subnormal inputs are legal and never flushed. NaN/Inf inputs are
+ *   outside the contract: no fault, unspecified values.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_INVALID_ARG = -1,  /* NULL pointer, negative size, ld too small  */
+  W8A8_ERR_UNSUPPORTED = -2,  /* K % 16 != 0, K > W8A8_K_MAX, odd ld        */
+  W8A8_ERR_MISALIGNED = -3,   /* pointer alignment below the requirement    */
+  W8A8_ERR_WORKSPACE = -4,    /* workspace NULL or smaller than required    */
+  W8A8_ERR_HIP = -5           /* a HIP launch failed; see w8a8_last_hip_error */
+} w8a8_status;
+
+/* Largest K whose worst-case accumulator 127*127*K fits in int32. */
+#define W8A8_K_MAX 133144
+/* Rows up to this count take the small-M (weight-streaming) path. */
+#define W8A8_SMALL_M 16
+
+/*
+ * Load-time per-output-channel weight quantisation ("Int8 Quantization"
+ * guide, "Overview": BF16/FP16 weights quantised at load time; Issue 5 probe,
+ * "Round two": unpacked int8 weights plus fp32 per-channel scales).
+ *   w        [N, ldw] bf16 (read)
+ *   wq       [N, K] int8, row stride K (written)
+ *   w_scale  [N] fp32 (written)
+ * The weight layout stays [N, K] with K contiguous: no transpose or repack
+ * is needed afterwards, both GEMM operands are K-contiguous.
+ */
+int w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                          int8_t* wq, float* w_scale, void* stream);
+
+/*
+ * Dynamic per-token activation quantisation (Issue 5 probe, "Round two":
+ * dynamic per-token symmetric int8 activations).
+ *   x        [M, ldx] bf16 (read)
+ *   xq       [M, K] int8, row stride K (written)
+ *   a_scale  [M] fp32 (written)
+ */
+int w8a8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                   int8_t* xq, float* a_scale, void* stream);
+
+/*
+ * Scaled int8 matrix product on pre-quantised activations (the second of the
+ * two ops of Issue 5 probe, "Round two": the int8 scaled-MM).
+ *   xq [M, K] int8 (row stride K), a_scale [M] fp32
+ *   wq [N, K] int8 (row stride K), w_scale [N] fp32
+ *   bias [N] bf16 or NULL
+ *   out [M, ldo] bf16 (written)
+ *   acc_debug [M, N] int32 (row stride N) or NULL: when given, the same
+ *     kernel also stores its raw int32 accumulators there (for parity checks).
+ */
+int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                   const int8_t* wq, const float* w_scale, int64_t N,
+                   const uint16_t* bias, uint16_t* out, int64_t ldo,
+                   int32_t* acc_debug, void* stream);
+
+/*
+ * The whole W8A8 linear: dynamic activation quantisation, int8 product and
+ * scale epilogue.
+ *   x [M, ldx] bf16; wq [N, K] int8; w_scale [N] fp32; bias [N] bf16 or NULL
+ *   out [M, ldo] bf16 (written)
+ *   workspace: device scratch of at least w8a8_linear_workspace_bytes(M,K,N)
+ *     bytes, 16-byte aligned, owned by the caller. After the call it holds the
+ *     quantised activations xq [M, K] int8 (row stride K) at byte offset 0 and
+ *     a_scale [M] fp32 at byte offset W8A8_ALIGN256(M*K), on both paths.
+ *   acc_debug [M, N] int32 or NULL, as in w8a8_scaled_mm.
+ * Path: M <= W8A8_SMALL_M (and K <= 8192) runs one fused weight-streaming
+ * kernel that quantises x on chip; otherwise the activation quantisation
+ * kernel runs first and the MFMA GEMM second. Both paths give bit-identical
+ * xq, a_scale, acc and out for the same row.
+ */
+int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                const int8_t* wq, const float* w_scale, int64_t N,
+                const uint16_t* bias, uint16_t* out, int64_t ldo,
+                void* workspace, size_t workspace_bytes,
+                int32_t* acc_debug, void* stream);
+
+#define W8A8_ALIGN256(b) ((((size_t)(b)) + 255u) & ~(size_t)255u)
+
+/* Workspace bytes w8a8_linear needs for this shape (0 if M == 0). */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/* Which kernels w8a8_linear runs for this shape: W8A8_PATH_SMALL_M (fused
+ * small-M kernel) or W8A8_PATH_GEMM (quantisation kernel + MFMA GEMM);
+ * W8A8_PATH_NONE for M == 0; a negative w8a8_status for invalid sizes. */
+#define W8A8_PATH_NONE 0
+#define W8A8_PATH_SMALL_M 1
+#define W8A8_PATH_GEMM 2
+int w8a8_linear_path(int64_t M, int64_t K, int64_t N);
+
+/* The GEMM tile configuration the MFMA kernel uses for this shape
+ * (BM rows of x by BN rows of W per workgroup), for checking kernel choice. */
+int w8a8_gemm_tile(int64_t M, int64_t K, int64_t N, int* bm, int* bn);
+
+/* Static text for a status code. */
+const char* w8a8_status_string(int status);
+
+/* hipError_t of the last failed launch on the calling thread (0 if none). */
+int w8a8_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

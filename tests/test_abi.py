@@ -1,0 +1,151 @@
+"""The C ABI of libw8a8 on the CPU: the library loads, exports every symbol
+include/w8a8.h declares, and rejects invalid arguments before launching
+anything (no GPU needed: every call here returns during validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_int8_dynamic_quant_amd as w8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+P = ctypes.c_void_p
+A = 0x10000          # a fake, 256-byte aligned device address (never dereferenced)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(w8a8_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert header_functions() == sorted(w8.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = w8.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_constants_match_header():
+    text = open(HEADER).read()
+    assert f"#define W8A8_K_MAX {w8.K_MAX}" in text
+    assert f"#define W8A8_SMALL_M {w8.SMALL_M}" in text
+    assert w8.K_MAX == (2**31 - 1) // (127 * 127)
+
+
+def q(fn, *args):
+    return getattr(w8.lib(), fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["w8a8_quant_act", "w8a8_quantize_weights"])
+def test_quant_validation(fn):
+    ok = (P(A), 4, 64, 64, P(A), P(A), None)
+    assert q(fn, P(A), -1, 64, 64, P(A), P(A), None) == w8.ERR_INVALID_ARG
+    for K in (0, 8, 24, 100, w8.K_MAX + 16):
+        assert q(fn, P(A), 4, K, 4096 * 64, P(A), P(A), None) == w8.ERR_UNSUPPORTED, K
+    assert q(fn, P(A), 4, -16, 64, P(A), P(A), None) == w8.ERR_INVALID_ARG
+    assert q(fn, P(A), 4, 64, 48, P(A), P(A), None) == w8.ERR_INVALID_ARG      # ld < K
+    assert q(fn, P(A), 4, 64, 68, P(A), P(A), None) == w8.ERR_UNSUPPORTED      # ld % 8
+    assert q(fn, None, 4, 64, 64, P(A), P(A), None) == w8.ERR_INVALID_ARG
+    assert q(fn, P(A), 4, 64, 64, None, P(A), None) == w8.ERR_INVALID_ARG
+    assert q(fn, P(A), 4, 64, 64, P(A), None, None) == w8.ERR_INVALID_ARG
+    assert q(fn, P(A + 2), 4, 64, 64, P(A), P(A), None) == w8.ERR_MISALIGNED
+    assert q(fn, P(A), 4, 64, 64, P(A + 8), P(A), None) == w8.ERR_MISALIGNED
+    assert q(fn, P(A), 4, 64, 64, P(A), P(A + 2), None) == w8.ERR_MISALIGNED
+    # M == 0 is a no-op, even with NULL buffers
+    assert q(fn, None, 0, 64, 64, None, None, None) == w8.OK
+    assert ok  # the valid call itself would launch; it is exercised on the GPU
+
+
+def test_scaled_mm_validation():
+    f = "w8a8_scaled_mm"
+    base = [P(A), P(A), 4, 64, P(A), P(A), 8, None, P(A), 8, None, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["xq", "sa", "M", "K", "wq", "sw", "N", "bias", "out", "ldo", "acc", "st"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(M=-1) == w8.ERR_INVALID_ARG
+    assert call(N=0) == w8.ERR_INVALID_ARG
+    assert call(K=40) == w8.ERR_UNSUPPORTED
+    assert call(K=w8.K_MAX + 16) == w8.ERR_UNSUPPORTED
+    assert call(ldo=7) == w8.ERR_INVALID_ARG
+    assert call(xq=None) == w8.ERR_INVALID_ARG
+    assert call(wq=None) == w8.ERR_INVALID_ARG
+    assert call(out=None) == w8.ERR_INVALID_ARG
+    assert call(sw=None) == w8.ERR_INVALID_ARG
+    assert call(sa=None) == w8.ERR_INVALID_ARG
+    assert call(xq=P(A + 4)) == w8.ERR_MISALIGNED
+    assert call(wq=P(A + 4)) == w8.ERR_MISALIGNED
+    assert call(sw=P(A + 2)) == w8.ERR_MISALIGNED
+    assert call(bias=P(A + 1)) == w8.ERR_MISALIGNED
+    assert call(acc=P(A + 2)) == w8.ERR_MISALIGNED
+    assert call(M=0, xq=None, sa=None, wq=None, sw=None, out=None) == w8.OK
+
+
+def test_linear_validation():
+    f = "w8a8_linear"
+    M, K, N = 32, 64, 8
+    ws = w8.workspace_bytes(M, K, N)
+    base = [P(A), M, K, K, P(A), P(A), N, None, P(A), N, P(A), ws, None, None]
+    names = ["x", "M", "K", "ldx", "wq", "sw", "N", "bias", "out", "ldo", "ws", "wsb", "acc", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(M=-3) == w8.ERR_INVALID_ARG
+    assert call(K=0) == w8.ERR_UNSUPPORTED
+    assert call(ldx=32) == w8.ERR_INVALID_ARG
+    assert call(ldx=68) == w8.ERR_UNSUPPORTED
+    assert call(x=None) == w8.ERR_INVALID_ARG
+    assert call(x=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(ws=None) == w8.ERR_WORKSPACE
+    assert call(wsb=ws - 1) == w8.ERR_WORKSPACE
+    assert call(ws=P(A + 4)) == w8.ERR_MISALIGNED
+    assert call(M=0, x=None, ws=None, wsb=0) == w8.OK
+
+
+def test_workspace_and_path_queries():
+    assert w8.workspace_bytes(0, 64, 8) == 0
+    assert w8.workspace_bytes(1, 64, 8) == 256 + 256
+    assert w8.workspace_bytes(4352, 3072, 9216) == 4352 * 3072 + 17408
+    assert w8.linear_path(0, 64, 8) == w8.PATH_NONE
+    for m in (1, 2, 8, 16):
+        assert w8.linear_path(m, 3072, 18432) == w8.PATH_SMALL_M
+    for m in (17, 32, 4352):
+        assert w8.linear_path(m, 3072, 18432) == w8.PATH_GEMM
+    # the small-M kernel keeps K in LDS: longer rows use the GEMM
+    assert w8.linear_path(1, 8192, 64) == w8.PATH_SMALL_M
+    assert w8.linear_path(1, 8208, 64) == w8.PATH_GEMM
+    assert w8.linear_path(4, 20, 8) == w8.ERR_UNSUPPORTED
+    assert w8.linear_path(-1, 64, 8) == w8.ERR_INVALID_ARG
+    bm, bn = w8.gemm_tile(4352, 3072, 9216)
+    assert bm >= 128 and bn >= 128
+
+
+def test_status_strings():
+    for s in (w8.OK, w8.ERR_INVALID_ARG, w8.ERR_UNSUPPORTED, w8.ERR_MISALIGNED,
+              w8.ERR_WORKSPACE, w8.ERR_HIP):
+        assert w8.status_string(s) and w8.status_string(s) != "unknown status"
+    assert w8.status_string(12345) == "unknown status"
+    assert q("w8a8_last_hip_error") == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        w8.quant_act(torch.zeros((2, 16), dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        w8.quant_act(torch.zeros((2, 16), dtype=torch.float32))

@@ -1,0 +1,143 @@
+// C ABI of libw8a8 (declared in include/w8a8.h): argument validation, path
+// dispatch and kernel launches on the caller's stream. Nothing is allocated
+// and nothing is kept between calls.
+#include <hip/hip_runtime.h>
+
+#include "../../include/w8a8.h"
+#include "w8a8_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_k(int64_t K) {
+  if (K < 0) return W8A8_ERR_INVALID_ARG;
+  if (K < 16 || (K % 16) != 0 || K > W8A8_K_MAX) return W8A8_ERR_UNSUPPORTED;
+  return W8A8_OK;
+}
+
+int check_bf16_ld(int64_t ld, int64_t K) {
+  if (ld < K) return W8A8_ERR_INVALID_ARG;
+  if (ld % 8 != 0) return W8A8_ERR_UNSUPPORTED;
+  return W8A8_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return W8A8_OK;
+  g_last_hip_error = (int)e;
+  return W8A8_ERR_HIP;
+}
+
+int quant_common(const uint16_t* x, int64_t R, int64_t K, int64_t ld, int8_t* q, float* scale,
+                 void* stream) {
+  if (R < 0) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(K)) return s;
+  if (int s = check_bf16_ld(ld, K)) return s;
+  if (R == 0) return W8A8_OK;
+  if (!x || !q || !scale) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return W8A8_ERR_MISALIGNED;
+  return hip_status(w8a8::launch_quant_rows(x, R, K, ld, q, scale, (hipStream_t)stream));
+}
+
+// Checks shared by the two GEMM entry points (everything but x / xq).
+int check_gemm(int64_t M, int64_t K, int64_t N, const int8_t* wq, const float* w_scale,
+               const uint16_t* bias, const uint16_t* out, int64_t ldo, const int32_t* acc_debug) {
+  if (M < 0 || N < 1) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(K)) return s;
+  if (ldo < N) return W8A8_ERR_INVALID_ARG;
+  if (M == 0) return W8A8_OK;
+  if (!wq || !w_scale || !out) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(out, 4)) return W8A8_ERR_MISALIGNED;
+  if (bias && !aligned(bias, 2)) return W8A8_ERR_MISALIGNED;
+  if (acc_debug && !aligned(acc_debug, 4)) return W8A8_ERR_MISALIGNED;
+  return W8A8_OK;
+}
+
+bool small_m_path(int64_t M, int64_t K) {
+  return M >= 1 && M <= W8A8_SMALL_M && K <= w8a8::kSmallMMaxK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wq,
+                          float* w_scale, void* stream) {
+  return quant_common(w, N, K, ldw, wq, w_scale, stream);
+}
+
+int w8a8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* xq,
+                   float* a_scale, void* stream) {
+  return quant_common(x, M, K, ldx, xq, a_scale, stream);
+}
+
+int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                   const int8_t* wq, const float* w_scale, int64_t N, const uint16_t* bias,
+                   uint16_t* out, int64_t ldo, int32_t* acc_debug, void* stream) {
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!xq || !a_scale) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(a_scale, 4)) return W8A8_ERR_MISALIGNED;
+  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo};
+  return hip_status(w8a8::launch_gemm(g, (hipStream_t)stream));
+}
+
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+  (void)N;
+  if (M <= 0 || K <= 0) return 0;
+  return W8A8_ALIGN256((size_t)M * (size_t)K) + W8A8_ALIGN256((size_t)M * sizeof(float));
+}
+
+int w8a8_linear_path(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || N < 1) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(K)) return s;
+  if (M == 0) return W8A8_PATH_NONE;
+  return small_m_path(M, K) ? W8A8_PATH_SMALL_M : W8A8_PATH_GEMM;
+}
+
+int w8a8_gemm_tile(int64_t M, int64_t K, int64_t N, int* bm, int* bn) {
+  if (M < 1 || N < 1 || !bm || !bn) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(K)) return s;
+  w8a8::gemm_pick_tile(M, N, K, bm, bn);
+  return W8A8_OK;
+}
+
+int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
+                int64_t ldo, void* workspace, size_t workspace_bytes, int32_t* acc_debug,
+                void* stream) {
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
+  if (int s = check_bf16_ld(ldx, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!x) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < w8a8_linear_workspace_bytes(M, K, N))
+    return W8A8_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return W8A8_ERR_MISALIGNED;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* a_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            W8A8_ALIGN256((size_t)M * (size_t)K));
+  hipStream_t st = (hipStream_t)stream;
+  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo};
+  if (small_m_path(M, K)) return hip_status(w8a8::launch_small_m(x, ldx, g, xq, a_scale, st));
+  if (int s = hip_status(w8a8::launch_quant_rows(x, M, K, ldx, xq, a_scale, st))) return s;
+  return hip_status(w8a8::launch_gemm(g, st));
+}
+
+const char* w8a8_status_string(int status) {
+  switch (status) {
+    case W8A8_OK: return "ok";
+    case W8A8_ERR_INVALID_ARG: return "invalid argument";
+    case W8A8_ERR_UNSUPPORTED: return "unsupported shape or leading dimension";
+    case W8A8_ERR_MISALIGNED: return "misaligned pointer";
+    case W8A8_ERR_WORKSPACE: return "workspace missing or too small";
+    case W8A8_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int w8a8_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch functions of libw8a8 (host side). Each enqueues kernels on
+// `stream` and returns the launch status; arguments are validated by the
+// C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Per-row symmetric int8 quantisation of R bf16 rows of length K.
+hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ldx,
+                             int8_t* q, float* scale, hipStream_t stream);
+
+struct GemmArgs {
+  const int8_t* xq;        // [M, K]
+  const float* a_scale;    // [M]
+  const int8_t* wq;        // [N, K]
+  const float* w_scale;    // [N]
+  const uint16_t* bias;    // [N] or nullptr
+  uint16_t* out;           // [M, ldo]
+  int32_t* acc_debug;      // [M, N] or nullptr
+  int64_t M, N, K, ldo;
+};
+
+// Bit 0: out rows allow 8-byte stores of four bf16 (out 8-byte aligned,
+// ldo % 4 == 0). Bit 1: acc_debug allows 16-byte stores (16-byte aligned,
+// N % 4 == 0). Lanes own four consecutive output columns starting at a
+// multiple of 4, so these conditions make every vector store aligned.
+inline int epilogue_vec_flags(const GemmArgs& a) {
+  const uintptr_t ob = reinterpret_cast<uintptr_t>(a.out);
+  const uintptr_t db = reinterpret_cast<uintptr_t>(a.acc_debug);
+  int f = 0;
+  if ((ob & 7) == 0 && (a.ldo & 3) == 0) f |= 1;
+  if ((db & 15) == 0 && (a.N & 3) == 0) f |= 2;
+  return f;
+}
+
+// Tile (BM x BN) the MFMA GEMM picks for a shape.
+void gemm_pick_tile(int64_t M, int64_t N, int64_t K, int* bm, int* bn);
+
+// int8 MFMA GEMM with the fused scale epilogue.
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// Small-M path: per-row activation quantisation on chip + weight-streaming
+// MFMA product + epilogue, one kernel. Also writes xq/a_scale to xq_out /
+// a_scale_out. Needs M <= 16 and K <= kSmallMMaxK.
+constexpr int64_t kSmallMMaxK = 8192;
+hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a,
+                          int8_t* xq_out, float* a_scale_out, hipStream_t stream);
+
+}  // namespace w8a8
