@@ -41,7 +41,22 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (3 times), the "
+                        "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
     return p.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.ones((n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -106,11 +121,15 @@ def main():
               "multi-GPU timing is out of scope)", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import numpy as np
     import torch
 
     import w8a8_int8_dynamic_quant_amd as w8
-    from synth_inputs import DIT_BLOCK, SPECS, make_linear_inputs
+    from synth_inputs import DIT_BLOCK, make_linear_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

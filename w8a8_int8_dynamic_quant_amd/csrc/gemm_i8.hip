@@ -9,19 +9,23 @@
 // Design (CDNA4):
 // * v_mfma_i32_16x16x64_i8. The MFMA "A" operand is a 16-row block of W and
 //   the "B" operand a 16-row block of xq (both K-contiguous, no transpose), so
-//   the accumulator lane layout gives each lane four consecutive output
-//   columns n of one output row m: the epilogue stores 8 bytes of bf16 per
-//   lane and per 16x16 block.
-// * Workgroup of 256 threads (4 waves) computes a BM x BN tile; each wave a
-//   WM x WN sub-tile held in registers as (WN/16)*(WM/16) MFMA blocks.
-// * K advances in stages of 128 bytes. Each stage of the W and xq panels is
-//   loaded from global memory with 16-byte loads (8 lanes per 128-byte row
-//   segment), kept in registers while the previous stage is multiplied, then
-//   written to the other half of a double-buffered LDS panel: one barrier per
-//   stage. 16-byte chunks are XOR-swizzled by (row & 7) so the ds_read_b128
-//   of 8 consecutive rows hit 8 distinct 16-byte bank groups.
-// * Out-of-range rows and K chunks load as zeros, so ragged M, N and K
-//   (K % 16 == 0) tails need no special path.
+//   each lane's accumulators are four consecutive output columns n of one
+//   output row m: the epilogue stores 8 bytes of bf16 per lane and block.
+// * A workgroup of NW waves computes a BM x BN tile, each wave a WM x WN
+//   sub-tile held as (WN/16)*(WM/16) MFMA blocks.
+// * Panels stream global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
+//   staging, no ds_write). One wave-instruction fills 1 KiB of LDS linearly
+//   by lane; each lane picks the global 16-byte chunk that belongs at its LDS
+//   slot, which realises an XOR swizzle of the 16-byte chunks so that the
+//   ds_read_b128 of 8 consecutive rows hit distinct banks.
+// * An S-stage LDS ring: loads for stage kt+S-1 are issued right after the
+//   barrier of stage kt; one barrier per stage; the wait before it only
+//   counts this stage's loads (exact s_waitcnt vmcnt).
+// * Out-of-range rows read as zeros through the buffer descriptor's bound;
+//   K-tail chunks are sent out of bounds, so ragged M, N and K need no branch.
+// * Tile order: every XCD (workgroups are dealt round-robin over the 8 XCDs)
+//   takes a contiguous range of a grouped tile order, so the tiles that run
+//   together on one XCD share W and xq panels in that XCD's L2.
 #include "w8a8_device.h"
 #include "w8a8_kernels.h"
 
@@ -29,61 +33,110 @@ namespace w8a8 {
 
 namespace {
 
-constexpr int kBK = 128;  // bytes of K per LDS stage (two MFMA k-steps of 64)
+constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor bound
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool HAS_BIAS>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, int vec_flags) {
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory ops (this wave's
+// newer panel loads) still in flight and every LDS read of this wave done.
+// gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in
+// bits 6:4 (7 = no wait), lgkmcnt in bits 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Swizzled position of logical 16-byte chunk c of LDS row `row`.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (BK == 128) return c ^ (row & 7);
+  else return c ^ ((row >> 1) & 3);
+}
+
+// (tm, tn) of the workgroup: XCD-contiguous ranges of a grouped order.
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int t = xcd * (T >> 3) + min(xcd, T & 7) + local;
+  constexpr int G = 8;                         // m-tiles per group
+  const int group = t / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int r = t - group * G * tiles_n;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArgs a, int tiles_m,
+                                                                         int tiles_n, int vec_flags) {
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 16, FN = WN / 16;
-  static_assert(FM >= 1 && FN >= 1 && BM % 32 == 0 && BN % 32 == 0, "tile shape");
-  constexpr int PA = BN / 32, PB = BM / 32;  // 16-byte loads per thread per stage
+  constexpr int CH = BK / 16;               // 16-byte chunks per LDS row
+  constexpr int RPI = 1024 / BK;            // LDS rows per wave-instruction
+  constexpr int JW = BN * BK / 1024, JX = BM * BK / 1024;
+  static_assert(JW % NW == 0 && JX % NW == 0, "panel loads must split evenly over waves");
+  constexpr int LW = JW / NW, LX = JX / NW, LPS = LW + LX;
+  static_assert(LPS * (S - 1) < 64, "vmcnt range");
+  constexpr int STAGE = (BM + BN) * BK;     // bytes per LDS stage (W rows then xq rows)
 
-  __shared__ __attribute__((aligned(16))) int8_t lds_w[2][BN * kBK];
-  __shared__ __attribute__((aligned(16))) int8_t lds_x[2][BM * kBK];
+  __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
-
-  const int tile = blockIdx.x;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t M = a.M, N = a.N, K = a.K;
 
-  // global -> register staging: thread covers row (tid/8 + 32p), chunk tid%8
-  const int ld_row = tid >> 3, ld_chunk = tid & 7;
-  uint4 rw[PA], rx[PB];
+  const uint32_t rows_w = (uint32_t)min<int64_t>(BN, N - n0);
+  const uint32_t rows_x = (uint32_t)min<int64_t>(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq + n0 * K, rows_w * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq + m0 * K, rows_x * (uint32_t)K);
 
-  auto load_stage = [&](int64_t k0) {
-    const int64_t kc = k0 + 16 * ld_chunk;
-    const bool kval = kc < K;
+  // Per-lane source of each of this wave's load instructions (stage-relative).
+  uint32_t off_w[LW], off_x[LX];
+  int kc_w[LW], kc_x[LX];
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const int64_t n = n0 + ld_row + 32 * p;
-      rw[p] = (kval && n < N) ? *reinterpret_cast<const uint4*>(a.wq + n * K + kc)
-                              : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < LW; ++j) {
+    const int row = (wave * LW + j) * RPI + lane / CH;
+    const int c = swz<BK>(row, lane % CH);
+    off_w[j] = (uint32_t)row * (uint32_t)K + 16u * c;
+    kc_w[j] = 16 * c;
+  }
+#pragma unroll
+  for (int j = 0; j < LX; ++j) {
+    const int row = (wave * LX + j) * RPI + lane / CH;
+    const int c = swz<BK>(row, lane % CH);
+    off_x[j] = (uint32_t)row * (uint32_t)K + 16u * c;
+    kc_x[j] = 16 * c;
+  }
+
+  auto issue = [&](int kt) {
+    int8_t* st = lds + (kt % S) * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const uint32_t off = (k0 + kc_w[j] < K) ? off_w[j] + k0 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, st + (wave * LW + j) * 1024, 16, off, 0, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int64_t m = m0 + ld_row + 32 * p;
-      rx[p] = (kval && m < M) ? *reinterpret_cast<const uint4*>(a.xq + m * K + kc)
-                              : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const int row = ld_row + 32 * p;
-      *reinterpret_cast<uint4*>(&lds_w[buf][row * kBK + 16 * swz(row, ld_chunk)]) = rw[p];
-    }
-#pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int row = ld_row + 32 * p;
-      *reinterpret_cast<uint4*>(&lds_x[buf][row * kBK + 16 * swz(row, ld_chunk)]) = rx[p];
+    for (int j = 0; j < LX; ++j) {
+      const uint32_t off = (k0 + kc_x[j] < K) ? off_x[j] + k0 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, st + BN * BK + (wave * LX + j) * 1024, 16, off,
+                                               0, 0, 0);
     }
   };
 
@@ -93,30 +146,33 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-  const int frag_row = lane & 15;   // row within a 16-row block
-  const int frag_grp = lane >> 4;   // which 16-byte group of the 64-byte k-step
+  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  const int nk = (int)((K + BK - 1) / BK);
 
-  const int nk = (int)((K + kBK - 1) / kBK);
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_stage((int64_t)(kt + 1) * kBK);
+    if (kt + S - 2 < nk) wait_vmcnt_lgkm0<LPS * (S - 2)>();
+    else wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+    const int8_t* sw = lds + (kt % S) * STAGE;
+    const int8_t* sx = sw + BN * BK;
 #pragma unroll
-    for (int s = 0; s < kBK / 64; ++s) {
+    for (int s = 0; s < BK / 64; ++s) {
       v4i fw[FN], fx[FM];
-      const int chunk = 4 * s + frag_grp;
+      const int c = 4 * s + frag_grp;
 #pragma unroll
       for (int i = 0; i < FN; ++i) {
         const int row = wave_n * WN + 16 * i + frag_row;
-        fw[i] = *reinterpret_cast<const v4i*>(&lds_w[cur][row * kBK + 16 * swz(row, chunk)]);
+        fw[i] = *reinterpret_cast<const v4i*>(sw + row * BK + 16 * swz<BK>(row, c));
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
         const int row = wave_m * WM + 16 * j + frag_row;
-        fx[j] = *reinterpret_cast<const v4i*>(&lds_x[cur][row * kBK + 16 * swz(row, chunk)]);
+        fx[j] = *reinterpret_cast<const v4i*>(sx + row * BK + 16 * swz<BK>(row, c));
       }
 #pragma unroll
       for (int i = 0; i < FN; ++i)
@@ -124,8 +180,6 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
         for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[i], fx[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_stage(cur ^ 1);
-    __syncthreads();
   }
 
   // Epilogue. Lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16], r=0..3.
@@ -180,18 +234,18 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(GemmArgs a, int tiles_m, i
   }
 }
 
-template <int BM, int BN, int WM_, int WN_>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   const int vec_flags = epilogue_vec_flags(a);
-  dim3 grid((unsigned)tiles), block(256);
+  dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
   if (a.bias)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM_, WN_, true>), grid, block, 0, stream, a,
-                       (int)tiles_m, vec_flags);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, true>), grid, block, 0,
+                       stream, a, (int)tiles_m, (int)tiles_n, vec_flags);
   else
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WM_, WN_, false>), grid, block, 0, stream, a,
-                       (int)tiles_m, vec_flags);
+    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, false>), grid, block, 0,
+                       stream, a, (int)tiles_m, (int)tiles_n, vec_flags);
   return hipGetLastError();
 }
 
@@ -209,10 +263,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   int bm, bn;
   gemm_pick_tile(a.M, a.N, a.K, &bm, &bn);
-  if (bm == 256) return launch_cfg<256, 256, 2, 2>(a, stream);
-  if (bm == 128) return launch_cfg<128, 128, 2, 2>(a, stream);
-  if (bm == 64) return launch_cfg<64, 64, 2, 2>(a, stream);
-  return launch_cfg<32, 64, 1, 4>(a, stream);
+  if (bm == 256) return launch_cfg<256, 256, 2, 2, 64, 4>(a, stream);
+  if (bm == 128) return launch_cfg<128, 128, 2, 2, 64, 4>(a, stream);
+  if (bm == 64) return launch_cfg<64, 64, 2, 2, 64, 4>(a, stream);
+  return launch_cfg<32, 64, 1, 4, 128, 4>(a, stream);
 }
 
 }  // namespace w8a8
