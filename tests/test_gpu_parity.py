@@ -262,3 +262,19 @@ def test_extreme_accumulators():
     w = np.full((N, K), 0x3F80, np.uint16)
     announce("extreme accumulators")
     _linear_case(x, w, None)
+
+
+def test_linear_subnormal_scales_and_outputs():
+    """Weights ~1e-41 (bf16 subnormals) give subnormal fp32 weight scales
+    (exact-division quantisation path) and bf16-subnormal outputs, on both
+    the small-M kernel and the GEMM."""
+    rng = np.random.default_rng(41)
+    K, N = 512, 320
+    w = to_bf16_bits(rng.normal(0.0, 1e-41, (N, K)))
+    assert np.any((w & 0x7F80) == 0) and np.any(w & 0x7FFF)
+    for M in (3, 70):
+        x = random_bf16(rng, (M, K))
+        announce(f"subnormal scales/outputs M={M}")
+        _, exp = _linear_case(x, w, None)
+        y = oracle.bf16_bits_to_f32(exp["y"])
+        assert np.any((np.abs(y) > 0) & (np.abs(y) < np.finfo(np.float32).tiny))

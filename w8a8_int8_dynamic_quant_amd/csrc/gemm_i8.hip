@@ -7,12 +7,18 @@
 //    and the fp32 per-channel weight scale)
 //
 // Design (CDNA4):
-// * v_mfma_i32_16x16x64_i8. The MFMA "A" operand is a 16-row block of W and
-//   the "B" operand a 16-row block of xq (both K-contiguous, no transpose), so
-//   each lane's accumulators are four consecutive output columns n of one
-//   output row m: the epilogue stores 8 bytes of bf16 per lane and block.
+// * v_mfma_i32_32x32x32_i8 (on gfx950 it runs at the full int8 rate from a
+//   single wave per SIMD; the 16x16x64 form sustains about half of it). The
+//   MFMA "A" operand is a 32-row block of W and the "B" operand a 32-row block
+//   of xq (both K-contiguous, no transpose), so each lane's 16 accumulators
+//   are four runs of four consecutive output columns n of one output row m:
+//   the epilogue stores 8 bytes of bf16 per run.
 // * A workgroup of NW waves computes a BM x BN tile, each wave a WM x WN
-//   sub-tile held as (WN/16)*(WM/16) MFMA blocks.
+//   sub-tile held as (WN/32)*(WM/32) MFMA blocks of 16 int32 per lane.
+// * K stages of 128 bytes, so every load instruction fetches whole 128-byte
+//   lines (8 rows x 128 B; half-line requests waste HBM bandwidth). Within a
+//   stage, the fragment reads of k-step s+1 are interleaved with the MFMAs of
+//   k-step s.
 // * Panels stream global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //   staging, no ds_write). One wave-instruction fills 1 KiB of LDS linearly
 //   by lane; each lane picks the global 16-byte chunk that belongs at its LDS
@@ -26,6 +32,9 @@
 // * Tile order: every XCD (workgroups are dealt round-robin over the 8 XCDs)
 //   takes a contiguous range of a grouped tile order, so the tiles that run
 //   together on one XCD share W and xq panels in that XCD's L2.
+#include <type_traits>
+#include <utility>
+
 #include "w8a8_device.h"
 #include "w8a8_kernels.h"
 
@@ -56,10 +65,13 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Swizzled position of logical 16-byte chunk c of LDS row `row`.
+// Swizzled position of logical 16-byte chunk c of LDS row `row`. The LDS
+// serves 16 lanes of a ds_read_b128 per cycle from 64 banks (256 bytes), and
+// the 16 lanes read rows r..r+15 of one chunk; keying the XOR on row >> 1
+// puts those 16 reads in 16 distinct 16-byte bank groups.
 template <int BK>
 __device__ __forceinline__ int swz(int row, int c) {
-  if constexpr (BK == 128) return c ^ (row & 7);
+  if constexpr (BK == 128) return c ^ ((row >> 1) & 7);
   else return c ^ ((row >> 1) & 3);
 }
 
@@ -78,23 +90,76 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = r / gm;
 }
 
+// Instruction order of one stage for the scheduler: the fragment reads of
+// k-step 0, then per k-step its MFMAs in groups, each group followed by one
+// fragment read of the next k-step and (in the first half of the stage) by
+// panel loads for a later stage.
+template <int KS, int KREADS, int KMFMA, int LOADS, int KSTEP>
+__device__ __forceinline__ void sched_kstep() {
+  constexpr int kPer = KMFMA / KREADS > 0 ? KMFMA / KREADS : 1;
+  constexpr int kGroups = KMFMA / kPer < KREADS ? KMFMA / kPer : KREADS;
+  constexpr int kIssueSteps = KS > 1 ? KS / 2 : 1;
+  constexpr int kLoadsHere = KSTEP < kIssueSteps ? (LOADS + kIssueSteps - 1) / kIssueSteps : 0;
+  constexpr int kLoadsPer = kLoadsHere / kGroups;
+  constexpr bool kRead = KSTEP + 1 < KS;
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+    if constexpr (kRead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if constexpr (kLoadsPer > 0) __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPer, 0);
+  }
+  if constexpr (KMFMA - kPer * kGroups > 0)
+    __builtin_amdgcn_sched_group_barrier(0x008, KMFMA - kPer * kGroups, 0);
+  if constexpr (kRead && KREADS - kGroups > 0)
+    __builtin_amdgcn_sched_group_barrier(0x100, KREADS - kGroups, 0);
+  if constexpr (kLoadsHere - kLoadsPer * kGroups > 0)
+    __builtin_amdgcn_sched_group_barrier(0x020, kLoadsHere - kLoadsPer * kGroups, 0);
+}
+
+template <int KS, int KREADS, int KMFMA, int LOADS, int... STEPS>
+__device__ __forceinline__ void sched_stage(std::integer_sequence<int, STEPS...>) {
+  __builtin_amdgcn_sched_group_barrier(0x100, KREADS, 0);
+  (sched_kstep<KS, KREADS, KMFMA, LOADS, STEPS>(), ...);
+}
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) packed low/high, one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const v2bf h = __builtin_convertvector((v2f){lo, hi}, v2bf);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArgs a, int tiles_m,
                                                                          int tiles_n, int vec_flags) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold 32x32 blocks");
+  static_assert(BK == 64 || BK == 128, "stage = 2 or 4 32-byte MFMA k-steps");
+  constexpr int KS = BK / 32;               // MFMA k-steps per stage
   constexpr int CH = BK / 16;               // 16-byte chunks per LDS row
   constexpr int RPI = 1024 / BK;            // LDS rows per wave-instruction
   constexpr int JW = BN * BK / 1024, JX = BM * BK / 1024;
   static_assert(JW % NW == 0 && JX % NW == 0, "panel loads must split evenly over waves");
   constexpr int LW = JW / NW, LX = JX / NW, LPS = LW + LX;
-  static_assert(LPS * (S - 1) < 64, "vmcnt range");
+  static_assert(S == 2, "two LDS stages (double buffer)");
+  static_assert(LPS < 64, "vmcnt range");
   constexpr int STAGE = (BM + BN) * BK;     // bytes per LDS stage (W rows then xq rows)
 
-  __shared__ __attribute__((aligned(1024))) int8_t lds[S * STAGE];
+  // Two separate arrays (not one indexed by kt % 2): the compiler can then
+  // prove that loads into one stage do not touch the other stage being read,
+  // and interleave them.
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[STAGE];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar
   const int wave_m = wave % WAVES_M, wave_n = wave / WAVES_M;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, tm, tn);
@@ -106,131 +171,188 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq + n0 * K, rows_w * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq + m0 * K, rows_x * (uint32_t)K);
 
-  // Per-lane source of each of this wave's load instructions (stage-relative).
+  // Load j of the wave fills LDS rows (wave*L + j)*RPI + lane/CH; lane takes
+  // the global chunk that belongs at its LDS slot under the swizzle.
   uint32_t off_w[LW], off_x[LX];
   int kc_w[LW], kc_x[LX];
 #pragma unroll
   for (int j = 0; j < LW; ++j) {
     const int row = (wave * LW + j) * RPI + lane / CH;
-    const int c = swz<BK>(row, lane % CH);
-    off_w[j] = (uint32_t)row * (uint32_t)K + 16u * c;
-    kc_w[j] = 16 * c;
+    kc_w[j] = 16 * swz<BK>(row, lane % CH);
+    off_w[j] = (uint32_t)row * (uint32_t)K + kc_w[j];
   }
 #pragma unroll
   for (int j = 0; j < LX; ++j) {
     const int row = (wave * LX + j) * RPI + lane / CH;
-    const int c = swz<BK>(row, lane % CH);
-    off_x[j] = (uint32_t)row * (uint32_t)K + 16u * c;
-    kc_x[j] = 16 * c;
+    kc_x[j] = 16 * swz<BK>(row, lane % CH);
+    off_x[j] = (uint32_t)row * (uint32_t)K + kc_x[j];
   }
-
-  auto issue = [&](int kt) {
-    int8_t* st = lds + (kt % S) * STAGE;
+  auto issue = [&](int kt, int8_t* st) {
     const int k0 = kt * BK;
+    const int klim = (int)K - k0;
 #pragma unroll
     for (int j = 0; j < LW; ++j) {
-      const uint32_t off = (k0 + kc_w[j] < K) ? off_w[j] + k0 : kOOB;
+      // chunks past K (only in a K-tail stage) go out of bounds, branch-free
+      const uint32_t keep = (uint32_t)((kc_w[j] - klim) >> 31);
+      const uint32_t off = ((off_w[j] + k0) & keep) | (kOOB & ~keep);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, st + (wave * LW + j) * 1024, 16, off, 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < LX; ++j) {
-      const uint32_t off = (k0 + kc_x[j] < K) ? off_x[j] + k0 : kOOB;
+      const uint32_t keep = (uint32_t)((kc_x[j] - klim) >> 31);
+      const uint32_t off = ((off_x[j] + k0) & keep) | (kOOB & ~keep);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, st + BN * BK + (wave * LX + j) * 1024, 16, off,
                                                0, 0, 0);
     }
   };
 
-  v4i acc[FN][FM];
+  v16i acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+    for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
 
-  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  // Fragment addresses: lane reads row 32*blk + lane%32 of its wave's rows,
+  // 16-byte chunk (2*ks + lane/32) of the stage. The swizzle depends on the
+  // low row bits only, so block b sits 32*BK*b bytes after block 0.
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  int fw_base[KS], fx_base[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    fw_base[ks] = (wave_n * WN + frag_row) * BK + 16 * swz<BK>(frag_row, 2 * ks + frag_half);
+    fx_base[ks] = BN * BK + (wave_m * WM + frag_row) * BK + 16 * swz<BK>(frag_row, 2 * ks + frag_half);
+  }
   const int nk = (int)((K + BK - 1) / BK);
 
+  // One stage: read the fragments of k-step 0, then run the MFMAs of each
+  // k-step with the next k-step's fragment reads spread between them. With
+  // ISSUE, the panel loads of stage kt+S-1 are spread over the first half of
+  // the MFMAs, so the memory path drains while the matrix core works.
+  auto stage = [&](int kt, const int8_t* st, int8_t* next, auto issue_tag) {
+    constexpr bool ISSUE = decltype(issue_tag)::value;
+    if constexpr (ISSUE) issue(kt + 1, next);
+    v4i fw[KS][FN], fx[KS][FM];
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + S - 2 < nk) wait_vmcnt_lgkm0<LPS * (S - 2)>();
-    else wait_vmcnt_lgkm0<0>();
-    stage_barrier();
-    if (kt + S - 1 < nk) issue(kt + S - 1);
-    const int8_t* sw = lds + (kt % S) * STAGE;
-    const int8_t* sx = sw + BN * BK;
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int s = 0; s < BK / 64; ++s) {
-      v4i fw[FN], fx[FM];
-      const int c = 4 * s + frag_grp;
+      for (int i = 0; i < FN; ++i)
+        fw[ks][i] = *reinterpret_cast<const v4i*>(st + fw_base[ks] + 32 * BK * i);
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wave_n * WN + 16 * i + frag_row;
-        fw[i] = *reinterpret_cast<const v4i*>(sw + row * BK + 16 * swz<BK>(row, c));
-      }
+      for (int j = 0; j < FM; ++j)
+        fx[ks][j] = *reinterpret_cast<const v4i*>(st + fx_base[ks] + 32 * BK * j);
+    }
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wave_m * WM + 16 * j + frag_row;
-        fx[j] = *reinterpret_cast<const v4i*>(sx + row * BK + 16 * swz<BK>(row, c));
-      }
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fw[i], fx[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[ks][i], fx[ks][j], acc[i][j], 0, 0, 0);
+    sched_stage<KS, FN + FM, FN * FM, ISSUE ? LPS : 0>(std::make_integer_sequence<int, KS>{});
+  };
+
+  // Double-buffered K loop: stage kt computes from one buffer while the
+  // loads of stage kt+1 fill the other; each stage begins with this wave's
+  // loads landed (vmcnt 0) and a barrier (everyone's loads landed, and
+  // everyone done reading the buffer about to be refilled).
+  issue(0, lds0);
+  int kt = 0;
+  for (; kt + 2 < nk; kt += 2) {
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    stage(kt, lds0, lds1, std::true_type{});
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    stage(kt + 1, lds1, lds0, std::true_type{});
+  }
+  if (kt + 1 < nk) {
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    stage(kt, lds0, lds1, std::true_type{});
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    stage(kt + 1, lds1, nullptr, std::false_type{});
+  } else {
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();
+    stage(kt, lds0, nullptr, std::false_type{});
   }
 
-  // Epilogue. Lane holds D[n = nb + 4*(lane/16) + r][m = mb + lane%16], r=0..3.
+  // Epilogue. Lane holds, for output row m = mb + lane%32, the columns
+  // n = nb + 8*q + 4*(lane/32) + r in acc element 4*q + r (q, r = 0..3).
+  // Branch-free: scales and bias come through buffer loads (zero past the
+  // end), stores go through buffer stores whose offset is sent out of bounds
+  // for columns >= N; rows >= M fall past the descriptor's bound.
+  __builtin_amdgcn_sched_barrier(0);
+  const int64_t ldo = a.ldo;
+  const __amdgpu_buffer_rsrc_t r_sa = make_rsrc(a.a_scale + m0, rows_x * 4u);
+  const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(a.w_scale + n0, rows_w * 4u);
+  const __amdgpu_buffer_rsrc_t r_out =
+      make_rsrc(a.out + m0 * ldo + n0, (uint32_t)(((int64_t)(rows_x - 1) * ldo + rows_w) * 2));
+  float sa[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
-    const int64_t m = m0 + wave_m * WM + 16 * j + (lane & 15);
-    if (m >= M) continue;
-    const float sa = a.a_scale[m];
+    const int ml = wave_m * WM + 32 * j + frag_row;
+    sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sa, ml * 4, 0, 0));
+  }
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int64_t n = n0 + wave_n * WN + 16 * i + 4 * (lane >> 4);
-      if (n >= N) continue;
-      const v4i c = acc[i][j];
-      if (n + 3 < N) {
-        const float sw0 = a.w_scale[n], sw1 = a.w_scale[n + 1];
-        const float sw2 = a.w_scale[n + 2], sw3 = a.w_scale[n + 3];
-        float b[4] = {0.f, 0.f, 0.f, 0.f};
-        if (HAS_BIAS) {
+  for (int i = 0; i < FN; ++i) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) b[r] = bf16_to_f32(a.bias[n + r]);
-        }
-        const uint32_t y0 = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[0], sa, sw0, b[0]));
-        const uint32_t y1 = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[1], sa, sw1, b[1]));
-        const uint32_t y2 = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[2], sa, sw2, b[2]));
-        const uint32_t y3 = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[3], sa, sw3, b[3]));
-        uint16_t* o = a.out + m * a.ldo + n;
+    for (int q = 0; q < 4; ++q) {
+      const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
+      float sw[4], b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sw[r] = __builtin_bit_cast(float,
+                                   __builtin_amdgcn_raw_buffer_load_b32(r_sw, (nl + r) * 4, 0, 0));
+      if constexpr (HAS_BIAS) {
+        const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          b[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_b, (nl + r) * 2, 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = wave_m * WM + 32 * j + frag_row;
+        float t[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = epilogue_f32<HAS_BIAS>(acc[i][j][4 * q + r], sa[j], sw[r], b[r]);
+        const uint32_t y01 = pack_bf16x2(t[0], t[1]), y23 = pack_bf16x2(t[2], t[3]);
+        const uint32_t base = (uint32_t)(ml * ldo + nl) * 2u;
         if (vec_flags & 1) {
-          *reinterpret_cast<uint2*>(o) = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
+          // N % 4 == 0 here, so the four columns are all valid or all invalid
+          const uint32_t off = (nl < (int)rows_w) ? base : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b64((v2u){y01, y23}, r_out, off, 0, 0);
         } else {
-          o[0] = (uint16_t)y0; o[1] = (uint16_t)y1; o[2] = (uint16_t)y2; o[3] = (uint16_t)y3;
-        }
-        if (a.acc_debug) {
-          int32_t* d = a.acc_debug + m * N + n;
-          if (vec_flags & 2) {
-            *reinterpret_cast<int4*>(d) = make_int4(c[0], c[1], c[2], c[3]);
-          } else {
-            d[0] = c[0]; d[1] = c[1]; d[2] = c[2]; d[3] = c[3];
-          }
-        }
-      } else {
+          const uint32_t y[4] = {y01 & 0xffffu, y01 >> 16, y23 & 0xffffu, y23 >> 16};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (n + r < N) {
-            const float b = HAS_BIAS ? bf16_to_f32(a.bias[n + r]) : 0.f;
-            const float t = epilogue_f32<HAS_BIAS>(c[r], sa, a.w_scale[n + r], b);
-            a.out[m * a.ldo + n + r] = (uint16_t)f32_to_bf16_rne(t);
-            if (a.acc_debug) a.acc_debug[m * N + n + r] = c[r];
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (nl + r < (int)rows_w) ? base + 2u * r : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)y[r], r_out, off, 0, 0);
           }
         }
       }
     }
+  }
+  if (a.acc_debug) {
+    const __amdgpu_buffer_rsrc_t r_acc =
+        make_rsrc(a.acc_debug + m0 * N + n0, (uint32_t)(((int64_t)(rows_x - 1) * N + rows_w) * 4));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = wave_m * WM + 32 * j + frag_row;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
+          const uint32_t base = (uint32_t)(ml * N + nl) * 4u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t off = (nl + r < (int)rows_w) ? base + 4u * r : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][4 * q + r], r_acc, off, 0, 0);
+          }
+        }
+      }
   }
 }
 
@@ -255,18 +377,16 @@ void gemm_pick_tile(int64_t M, int64_t N, int64_t K, int* bm, int* bn) {
   (void)K;
   if (M >= 512 && N >= 512) { *bm = 256; *bn = 256; return; }
   if (M >= 128) { *bm = 128; *bn = 128; return; }
-  if (M > 32) { *bm = 64; *bn = 64; return; }
-  *bm = 32; *bn = 64;
+  *bm = 64; *bn = 64;
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
   int bm, bn;
   gemm_pick_tile(a.M, a.N, a.K, &bm, &bn);
-  if (bm == 256) return launch_cfg<256, 256, 2, 2, 64, 4>(a, stream);
-  if (bm == 128) return launch_cfg<128, 128, 2, 2, 64, 4>(a, stream);
-  if (bm == 64) return launch_cfg<64, 64, 2, 2, 64, 4>(a, stream);
-  return launch_cfg<32, 64, 1, 4, 128, 4>(a, stream);
+  if (bm == 256) return launch_cfg<256, 256, 2, 2, 128, 2>(a, stream);
+  if (bm == 128) return launch_cfg<128, 128, 2, 2, 128, 2>(a, stream);
+  return launch_cfg<64, 64, 2, 2, 64, 2>(a, stream);
 }
 
 }  // namespace w8a8
