@@ -150,7 +150,8 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None, check_ws=True):
     return stats, exp
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (17, 33, 64), (33, 67, 80),
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (4, 100, 8192), (16, 70, 8192),
+                                   (2, 129, 8208), (17, 33, 64), (33, 67, 80),
                                    (67, 17, 208), (16, 300, 112), (65, 129, 1040),
                                    (130, 260, 528), (257, 513, 256), (300, 700, 1296)])
 @pytest.mark.parametrize("with_bias", [False, True])

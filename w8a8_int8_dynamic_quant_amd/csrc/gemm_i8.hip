@@ -157,6 +157,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   // and interleave them.
   __shared__ __attribute__((aligned(1024))) int8_t lds0[STAGE];
   __shared__ __attribute__((aligned(1024))) int8_t lds1[STAGE];
+  // the tile's activation scales, weight scales and bias, for the epilogue
+  __shared__ __attribute__((aligned(16))) float lds_sa[BM];
+  __shared__ __attribute__((aligned(16))) float lds_sw[BN];
+  __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar
@@ -170,6 +174,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   const uint32_t rows_x = (uint32_t)min<int64_t>(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq + n0 * K, rows_w * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq + m0 * K, rows_x * (uint32_t)K);
+
+  // Scales and bias of the tile into LDS (zero past M / N); the first stage
+  // barrier of the K loop makes them visible to every wave.
+  {
+    const __amdgpu_buffer_rsrc_t r_sa = make_rsrc(a.a_scale + m0, rows_x * 4u);
+    const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(a.w_scale + n0, rows_w * 4u);
+    for (int t = tid; t < BM; t += 64 * NW)
+      lds_sa[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sa, t * 4, 0, 0));
+    for (int t = tid; t < BN; t += 64 * NW)
+      lds_sw[t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sw, t * 4, 0, 0));
+    if constexpr (HAS_BIAS) {
+      const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
+      for (int t = tid; t < BN; t += 64 * NW)
+        lds_b[t] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_b, t * 2, 0, 0));
+    }
+  }
 
   // Load j of the wave fills LDS rows (wave*L + j)*RPI + lane/CH; lane takes
   // the global chunk that belongs at its LDS slot under the swizzle.
@@ -285,31 +305,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   // for columns >= N; rows >= M fall past the descriptor's bound.
   __builtin_amdgcn_sched_barrier(0);
   const int64_t ldo = a.ldo;
-  const __amdgpu_buffer_rsrc_t r_sa = make_rsrc(a.a_scale + m0, rows_x * 4u);
-  const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(a.w_scale + n0, rows_w * 4u);
   const __amdgpu_buffer_rsrc_t r_out =
       make_rsrc(a.out + m0 * ldo + n0, (uint32_t)(((int64_t)(rows_x - 1) * ldo + rows_w) * 2));
   float sa[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
     const int ml = wave_m * WM + 32 * j + frag_row;
-    sa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sa, ml * 4, 0, 0));
+    sa[j] = lds_sa[ml];
+  }
+  // Output tile staged through LDS (free after the K loop) when rows can be
+  // written with 16-byte stores: each lane's four bf16 go to LDS, then every
+  // thread writes 16 contiguous bytes of a row, so a wave stores two whole
+  // 512-byte row segments per instruction. Layout: tile row r (BN*2 bytes),
+  // 16-byte chunk c stored at chunk c ^ (r & 31), which keeps both the
+  // column-wise writes and the row-wise reads free of bank conflicts.
+  constexpr bool kStageOut = (BN * 2 == 512) && (BM * BN * 2 <= 2 * STAGE);
+  const bool stage_out = kStageOut && (vec_flags & 4);
+  if (stage_out) {
+    wait_vmcnt_lgkm0<0>();
+    stage_barrier();                      // every wave is done reading the K stages
   }
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
-      float sw[4], b[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sw[r] = __builtin_bit_cast(float,
-                                   __builtin_amdgcn_raw_buffer_load_b32(r_sw, (nl + r) * 4, 0, 0));
+      const float4 sw4 = *reinterpret_cast<const float4*>(&lds_sw[nl]);
+      const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+      float b[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (HAS_BIAS) {
-        const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          b[r] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_b, (nl + r) * 2, 0, 0));
+        const float4 b4 = *reinterpret_cast<const float4*>(&lds_b[nl]);
+        b[0] = b4.x; b[1] = b4.y; b[2] = b4.z; b[3] = b4.w;
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
@@ -318,6 +344,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
 #pragma unroll
         for (int r = 0; r < 4; ++r) t[r] = epilogue_f32<HAS_BIAS>(acc[i][j][4 * q + r], sa[j], sw[r], b[r]);
         const uint32_t y01 = pack_bf16x2(t[0], t[1]), y23 = pack_bf16x2(t[2], t[3]);
+        if (kStageOut && stage_out) {
+          const int c = nl >> 3;                         // 16-byte chunk of the row
+          int8_t* rowp = (ml < BM / 2 ? lds0 + ml * 512 : lds1 + (ml - BM / 2) * 512);
+          *reinterpret_cast<v2u*>(rowp + 16 * (c ^ (ml & 31)) + 8 * frag_half) = (v2u){y01, y23};
+          continue;
+        }
         const uint32_t base = (uint32_t)(ml * ldo + nl) * 2u;
         if (vec_flags & 1) {
           // N % 4 == 0 here, so the four columns are all valid or all invalid
@@ -332,6 +364,21 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
           }
         }
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (kStageOut && stage_out) {
+    __syncthreads();
+    constexpr int kThreads = 64 * NW;
+    constexpr int kRowsPerPass = kThreads / 32;
+    const int c = tid & 31;
+#pragma unroll 4
+    for (int r = tid >> 5; r < BM; r += kRowsPerPass) {
+      const int8_t* rowp = (r < BM / 2 ? lds0 + r * 512 : lds1 + (r - BM / 2) * 512);
+      const v4i v = *reinterpret_cast<const v4i*>(rowp + 16 * (c ^ (r & 31)));
+      // N % 8 == 0 here: the eight columns of a chunk are all valid or not
+      const uint32_t off = (8 * c < (int)rows_w) ? (uint32_t)(r * ldo + 8 * c) * 2u : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(v, r_out, off, 0, 0);
     }
   }
   if (a.acc_debug) {

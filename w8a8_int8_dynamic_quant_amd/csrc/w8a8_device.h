@@ -39,55 +39,68 @@ __device__ __forceinline__ float row_scale(uint32_t amax_bits16) {
   return bf16_to_f32(amax_bits16) / 127.0f;
 }
 
-// Rounds fl32(x / s) half to even and clamps to [-127, 127], where
-// r = fl32(1 / s) and s is a normal fp32 number.
+// Quantisation of one value: round(fl32(x / s)) half to even, clamped to
+// [-127, 127], computed as rint(t) with t = fl32(x * r), r = fl32(1 / s),
+// for a normal s.
 //
-// t = fl32(x * r) differs from the exact quotient Q = x/s by at most
-// |Q|(2u + u^2) and fl32(Q) differs from Q by at most |Q|u (u = 2^-24).
-// |Q| <= amax/s <= 127 / (1 - u), so |t - fl32(Q)| < 2.3e-5 < 2^-15. If t is
-// farther than 2^-15 from every half-integer, no rounding boundary lies
-// between t and fl32(Q) and rint(t) == rint(fl32(Q)). Otherwise the exact
-// division is taken. (t - rint(t) is exact by Sterbenz's lemma.)
-__device__ __forceinline__ int quant_fast(float x, float s, float r) {
-  float t = x * r;
-  float rt = __builtin_rintf(t);
-  float d = __builtin_fabsf(t - rt);
-  if (__builtin_fabsf(0.5f - d) <= 0x1p-15f) rt = __builtin_rintf(x / s);
-  rt = __builtin_fminf(__builtin_fmaxf(rt, -127.0f), 127.0f);
-  return (int)rt;
+// t differs from the exact quotient Q = x/s by at most |Q|(2u + u^2) and
+// fl32(Q) differs from Q by at most |Q|u (u = 2^-24). |Q| <= amax/s <=
+// 127 / (1 - u), so |t - fl32(Q)| < 2.3e-5 < 2^-15. If t is farther than
+// 2^-15 from every half-integer, no rounding boundary lies between t and
+// fl32(Q) and rint(t) == rint(fl32(Q)). Otherwise (`near` is set) the caller
+// redoes the element with the IEEE division. (t - rint(t) is exact by
+// Sterbenz's lemma, so the distance test itself does not round.)
+__device__ __forceinline__ float quant_mul(float x, float r, bool& near) {
+  const float t = x * r;
+  const float rt = __builtin_rintf(t);
+  const float d = __builtin_fabsf(t - rt);
+  near = __builtin_fabsf(0.5f - d) <= 0x1p-15f;
+  return rt;
 }
 
-// Exact route for every element: one IEEE division per element. Used for
+// Exact route: one IEEE division. Used near rounding boundaries and for
 // rows whose scale is subnormal (1/s would overflow or lose precision).
-__device__ __forceinline__ int quant_div(float x, float s) {
-  float rt = __builtin_rintf(x / s);
-  rt = __builtin_fminf(__builtin_fmaxf(rt, -127.0f), 127.0f);
-  return (int)rt;
+__device__ __forceinline__ float quant_div(float x, float s) { return __builtin_rintf(x / s); }
+
+__device__ __forceinline__ uint32_t clamp_pack4(float a, float b, float c, float d) {
+  const int ia = (int)__builtin_amdgcn_fmed3f(a, -127.0f, 127.0f);
+  const int ib = (int)__builtin_amdgcn_fmed3f(b, -127.0f, 127.0f);
+  const int ic = (int)__builtin_amdgcn_fmed3f(c, -127.0f, 127.0f);
+  const int id = (int)__builtin_amdgcn_fmed3f(d, -127.0f, 127.0f);
+  return (uint32_t)(ia & 0xff) | ((uint32_t)(ib & 0xff) << 8) | ((uint32_t)(ic & 0xff) << 16) |
+         ((uint32_t)id << 24);
 }
 
-// Quantises one bf16 value given the row's scale s and r = 1/s. A zero scale
-// (all-zero row) gives 0; subnormal scales take the division route.
-__device__ __forceinline__ int quant_one(uint32_t bits16, float s, float r, bool exact_div) {
-  float x = bf16_to_f32(bits16);
-  if (exact_div) return quant_div(x, s);
-  return quant_fast(x, s, r);
-}
-
-// Quantises eight bf16 values (one 16-byte load) into eight int8 values
-// packed little-endian in a uint2.
+// Quantises eight bf16 values (one 16-byte load) with scale s (r = 1/s) into
+// eight int8 packed little-endian in a uint2. A zero scale (all-zero row)
+// gives zeros. The division fallback is taken for the whole chunk, once per
+// wave, only when some lane has a value near a rounding boundary (or the
+// scale is subnormal), so the common path has no per-element branch.
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bool exact_div) {
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out[2] = {0u, 0u};
-  if (!zero) {
+  if (zero) return make_uint2(0u, 0u);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8], q[8];
+  bool any_near = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int lo = quant_one(w[i] & 0xffffu, s, r, exact_div);
-      int hi = quant_one(w[i] >> 16, s, r, exact_div);
-      uint32_t pair = (uint32_t)(lo & 0xff) | ((uint32_t)(hi & 0xff) << 8);
-      out[i >> 1] |= pair << ((i & 1) * 16);
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bool near;
+    q[i] = quant_mul(x[i], r, near);
+    any_near |= near;
+  }
+  if (__builtin_amdgcn_ballot_w64(any_near || exact_div)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bool near;
+      quant_mul(x[i], r, near);
+      if (near || exact_div) q[i] = quant_div(x[i], s);
     }
   }
-  return make_uint2(out[0], out[1]);
+  return make_uint2(clamp_pack4(q[0], q[1], q[2], q[3]), clamp_pack4(q[4], q[5], q[6], q[7]));
 }
 
 __device__ __forceinline__ uint32_t absmax_bits8(uint4 v, uint32_t m) {

@@ -24,15 +24,18 @@ struct GemmArgs {
 };
 
 // Bit 0: out rows allow 8-byte stores of four bf16 (out 8-byte aligned,
-// ldo % 4 == 0). Bit 1: acc_debug allows 16-byte stores (16-byte aligned,
-// N % 4 == 0). Lanes own four consecutive output columns starting at a
-// multiple of 4, so these conditions make every vector store aligned.
+// ldo % 4 == 0, N % 4 == 0). Bit 1: acc_debug allows 16-byte stores
+// (16-byte aligned, N % 4 == 0). Bit 2: out rows allow 16-byte stores of
+// eight bf16 (out 16-byte aligned, ldo % 8 == 0, N % 8 == 0). Lanes own
+// column groups that start at multiples of the store width, so these
+// conditions make every vector store aligned and all-or-nothing at N.
 inline int epilogue_vec_flags(const GemmArgs& a) {
   const uintptr_t ob = reinterpret_cast<uintptr_t>(a.out);
   const uintptr_t db = reinterpret_cast<uintptr_t>(a.acc_debug);
   int f = 0;
-  if ((ob & 7) == 0 && (a.ldo & 3) == 0) f |= 1;
+  if ((ob & 7) == 0 && (a.ldo & 3) == 0 && (a.N & 3) == 0) f |= 1;
   if ((db & 15) == 0 && (a.N & 3) == 0) f |= 2;
+  if ((ob & 15) == 0 && (a.ldo & 7) == 0 && (a.N & 7) == 0) f |= 4;
   return f;
 }
 
