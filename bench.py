@@ -81,17 +81,23 @@ def load_traffic(gemm_launch_ops):
     return c.get("hbm_bytes_per_launch_avg")
 
 
-def cpu_baseline(inputs, wq_host):
-    """The oracle, as it stands, on one whole step (all five linears)."""
+def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
+    """The oracle, as it stands, on whole steps (all five linears), repeated
+    until at least `min_seconds` of CPU work."""
     import numpy as np
 
     import oracle
     ops = 0
+    steps = 0
     t0 = time.perf_counter()
-    for name, d in inputs.items():
-        wq, sw = wq_host[name]
-        oracle.linear(d["x"], wq, sw, d["bias"])
-        ops += 2 * d["M"] * d["N"] * d["K"]
+    while True:
+        for name, d in inputs.items():
+            wq, sw = wq_host[name]
+            oracle.linear(d["x"], wq, sw, d["bias"])
+            ops += 2 * d["M"] * d["N"] * d["K"]
+        steps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     dt = time.perf_counter() - t0
     threads = None
     try:
@@ -104,7 +110,7 @@ def cpu_baseline(inputs, wq_host):
         "unit": "TOPS",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
-        "sample": "one whole step: the 4 DiT block linears at M=4352 and the M=1 "
+        "sample": f"{steps} whole step(s): the 4 DiT block linears at M=4352 and the M=1 "
                   "modulation projection (quantise, exact int GEMM, fp32 epilogue)",
         "seconds": dt,
         "host_cpus": os.cpu_count(),
