@@ -274,10 +274,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   // Double-buffered K loop: stage kt computes from one buffer while the
   // loads of stage kt+1 fill the other; each stage begins with this wave's
   // loads landed (vmcnt 0) and a barrier (everyone's loads landed, and
-  // everyone done reading the buffer about to be refilled).
+  // everyone done reading the buffer about to be refilled). The last stage's
+  // "next" loads have K offsets past the end, so they only write zeros into
+  // the idle buffer, which keeps every stage body identical.
   issue(0, lds0);
   int kt = 0;
-  for (; kt + 2 < nk; kt += 2) {
+  for (; kt + 1 < nk; kt += 2) {
     wait_vmcnt_lgkm0<0>();
     stage_barrier();
     stage(kt, lds0, lds1, std::true_type{});
@@ -285,17 +287,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
     stage_barrier();
     stage(kt + 1, lds1, lds0, std::true_type{});
   }
-  if (kt + 1 < nk) {
+  if (kt < nk) {
     wait_vmcnt_lgkm0<0>();
     stage_barrier();
     stage(kt, lds0, lds1, std::true_type{});
-    wait_vmcnt_lgkm0<0>();
-    stage_barrier();
-    stage(kt + 1, lds1, nullptr, std::false_type{});
-  } else {
-    wait_vmcnt_lgkm0<0>();
-    stage_barrier();
-    stage(kt, lds0, nullptr, std::false_type{});
   }
 
   // Epilogue. Lane holds, for output row m = mb + lane%32, the columns
@@ -319,55 +314,43 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   // 512-byte row segments per instruction. Layout: tile row r (BN*2 bytes),
   // 16-byte chunk c stored at chunk c ^ (r & 31), which keeps both the
   // column-wise writes and the row-wise reads free of bank conflicts.
+  // The store path is chosen once per workgroup; each path is branch-free.
   constexpr bool kStageOut = (BN * 2 == 512) && (BM * BN * 2 <= 2 * STAGE);
-  const bool stage_out = kStageOut && (vec_flags & 4);
-  if (stage_out) {
+  // visit(i, q, j, nl, ml, y01, y23) for every group of four outputs
+  auto for_each_out = [&](auto&& visit) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
+        const float4 sw4 = *reinterpret_cast<const float4*>(&lds_sw[nl]);
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS) {
+          const float4 bb = *reinterpret_cast<const float4*>(&lds_b[nl]);
+          b4[0] = bb.x; b4[1] = bb.y; b4[2] = bb.z; b4[3] = bb.w;
+        }
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int ml = wave_m * WM + 32 * j + frag_row;
+          const v16i& c = acc[i][j];
+          const float t0 = epilogue_f32<HAS_BIAS>(c[4 * q + 0], sa[j], sw4.x, b4[0]);
+          const float t1 = epilogue_f32<HAS_BIAS>(c[4 * q + 1], sa[j], sw4.y, b4[1]);
+          const float t2 = epilogue_f32<HAS_BIAS>(c[4 * q + 2], sa[j], sw4.z, b4[2]);
+          const float t3 = epilogue_f32<HAS_BIAS>(c[4 * q + 3], sa[j], sw4.w, b4[3]);
+          visit(nl, ml, pack_bf16x2(t0, t1), pack_bf16x2(t2, t3));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  if (kStageOut && (vec_flags & 4)) {
     wait_vmcnt_lgkm0<0>();
     stage_barrier();                      // every wave is done reading the K stages
-  }
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
-      const float4 sw4 = *reinterpret_cast<const float4*>(&lds_sw[nl]);
-      const float sw[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
-      float b[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (HAS_BIAS) {
-        const float4 b4 = *reinterpret_cast<const float4*>(&lds_b[nl]);
-        b[0] = b4.x; b[1] = b4.y; b[2] = b4.z; b[3] = b4.w;
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int ml = wave_m * WM + 32 * j + frag_row;
-        float t[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] = epilogue_f32<HAS_BIAS>(acc[i][j][4 * q + r], sa[j], sw[r], b[r]);
-        const uint32_t y01 = pack_bf16x2(t[0], t[1]), y23 = pack_bf16x2(t[2], t[3]);
-        if (kStageOut && stage_out) {
-          const int c = nl >> 3;                         // 16-byte chunk of the row
-          int8_t* rowp = (ml < BM / 2 ? lds0 + ml * 512 : lds1 + (ml - BM / 2) * 512);
-          *reinterpret_cast<v2u*>(rowp + 16 * (c ^ (ml & 31)) + 8 * frag_half) = (v2u){y01, y23};
-          continue;
-        }
-        const uint32_t base = (uint32_t)(ml * ldo + nl) * 2u;
-        if (vec_flags & 1) {
-          // N % 4 == 0 here, so the four columns are all valid or all invalid
-          const uint32_t off = (nl < (int)rows_w) ? base : kOOB;
-          __builtin_amdgcn_raw_buffer_store_b64((v2u){y01, y23}, r_out, off, 0, 0);
-        } else {
-          const uint32_t y[4] = {y01 & 0xffffu, y01 >> 16, y23 & 0xffffu, y23 >> 16};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t off = (nl + r < (int)rows_w) ? base + 2u * r : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)y[r], r_out, off, 0, 0);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (kStageOut && stage_out) {
+    for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+      const int c = nl >> 3;                                 // 16-byte chunk of the row
+      int8_t* rowp = (ml < BM / 2 ? lds0 + ml * 512 : lds1 + (ml - BM / 2) * 512);
+      *reinterpret_cast<v2u*>(rowp + 16 * (c ^ (ml & 31)) + 8 * frag_half) = (v2u){y01, y23};
+    });
     __syncthreads();
     constexpr int kThreads = 64 * NW;
     constexpr int kRowsPerPass = kThreads / 32;
@@ -380,6 +363,22 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
       const uint32_t off = (8 * c < (int)rows_w) ? (uint32_t)(r * ldo + 8 * c) * 2u : kOOB;
       __builtin_amdgcn_raw_buffer_store_b128(v, r_out, off, 0, 0);
     }
+  } else if (vec_flags & 1) {
+    for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+      // N % 4 == 0 here, so the four columns are all valid or all invalid
+      const uint32_t off = (nl < (int)rows_w) ? (uint32_t)(ml * ldo + nl) * 2u : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b64((v2u){y01, y23}, r_out, off, 0, 0);
+    });
+  } else {
+    for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+      const uint32_t base = (uint32_t)(ml * ldo + nl) * 2u;
+      const uint32_t y[4] = {y01 & 0xffffu, y01 >> 16, y23 & 0xffffu, y23 >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t off = (nl + r < (int)rows_w) ? base + 2u * r : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)y[r], r_out, off, 0, 0);
+      }
+    });
   }
   if (a.acc_debug) {
     const __amdgpu_buffer_rsrc_t r_acc =
