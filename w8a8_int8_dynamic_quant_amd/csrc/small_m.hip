@@ -6,19 +6,27 @@
 // test_diffusion_transformer_quant.py). Here they are served by a kernel
 // whose cost is streaming the int8 weight once from HBM.
 //
-// Workgroup of 4 waves, 64 weight rows; each wave owns 16 rows over the
-// whole K:
-//  0. the wave issues its first weight loads at once, so they are in flight
-//     while the activations are quantised;
+// Workgroup of 4 waves, 32 weight rows; each wave owns 8 rows over the whole
+// K, read in 128-byte windows:
 //  1. the M activation rows are quantised on chip (per-row amax, scale =
-//     amax/127, exact half-to-even rounding) into LDS as int8 [16][K] (rows
-//     M..15 are left unwritten: their output columns are discarded);
-//     workgroup 0 also writes xq and a_scale out for the caller;
-//  2. the wave streams its 16 weight rows: each 64-byte k-step of the 16
-//     rows is the "A" operand of v_mfma_i32_16x16x64_i8, loaded straight from
-//     HBM into registers through a bounded buffer descriptor (rows past N and
-//     chunks past K read as zero, no branches), kDepth batches ahead; the
-//     activations are the "B" operand, read from LDS;
+//     amax/127, exact half-to-even rounding) into LDS as int8 [M][K];
+//     workgroup 0 also writes xq and a_scale out for the caller. The rows
+//     are read before any weight window is requested: vector-memory requests
+//     of the whole chip share the same queues, and the few KiB of x requested
+//     behind the weight stream would arrive last. With M <= 4 (one row per
+//     wave) the quantisation itself then runs while the weights stream;
+//  2. the wave requests up to kD 128-byte windows of its rows at once
+//     (one buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte
+//     chunk l/8, so every instruction fetches 8 whole 128-byte lines).
+//     Each window is one v_mfma_i32_16x16x64_i8 per 8 tokens. The loaded
+//     layout is the MFMA "A" layout if A-row i is read as weight row i%8 at
+//     chunk parity i/8: lane l holds A[l%16][k-group l/16] = row l%8, chunk
+//     2*(l/16) + (l/8)%2 = l/8. The "B" operand is built the same way from
+//     LDS: column j = token j%8 at chunk parity j/8. Then
+//     D[n][t] + D[n+8][t+8] is the dot product of weight row n and token t
+//     over the window (the other two blocks of D are unused). The loads are
+//     refilled kD windows ahead through a buffer descriptor bounded at the
+//     wave's rows, so rows past N and chunks past K read as zero, branch-free;
 //  3. the epilogue is the GEMM's, in the same fp32 order, so a row gives
 //     bit-identical results on either path.
 #include "w8a8_device.h"
@@ -29,9 +37,15 @@ namespace w8a8 {
 namespace {
 
 constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor bound
-constexpr int kU = 4;                    // k-steps (64 bytes each) per load batch
-constexpr int kDepth = 3;                // load batches in flight per wave
-constexpr int kQ = 8;                    // 16-byte chunks per lane per quantisation batch
+constexpr int kD = 24;                   // 128-byte windows in flight per wave
+constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisation batch
+constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
+
+// Work split of a launch: ONE_ROW: M <= 4 and K <= kShortK (a wave quantises
+// at most one activation row, overlapped with the weight stream); SHORT:
+// K <= kShortK; LONG: longer rows (read twice for quantisation, weight
+// windows refilled as they are consumed).
+enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -44,17 +58,86 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 }
 
 // LDS row stride for the quantised activations: K rounded up to whole
-// k-steps plus 16 bytes, an odd multiple of 16 modulo 256, so the 16 rows
-// read by one ds_read_b128 land in distinct banks.
-__host__ __device__ inline int xs_stride(int64_t K) {
-  const int kp = (int)((K + 63) / 64) * 64;
-  return kp + 16;
+// 128-byte windows plus 32 bytes. One quarter-wave of the "B" read takes 8
+// tokens x 2 adjacent 16-byte chunks; with the stride an odd multiple of 32
+// modulo 256 after the padding (or 32 itself), those 16 chunks fall into 16
+// distinct 16-byte bank groups.
+__host__ __device__ inline int xs_stride(int64_t K) { return (int)((K + 127) / 128) * 128 + 32; }
+
+// Barrier on LDS traffic only (lgkmcnt 0, no fence): loads of weight windows
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0); vmcnt and expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
-template <bool HAS_BIAS>
-__global__ __launch_bounds__(256) void small_m_kernel(const uint16_t* __restrict__ x, int64_t ldx,
-                                                      GemmArgs a, int8_t* __restrict__ xq_out,
-                                                      float* __restrict__ sa_out, int vec_flags) {
+// Quantises the row chunks held in v (chunk lane + 64*u of the row, u < kQ)
+// with the row's scale; returns the scale.
+__device__ __forceinline__ float quantise_regs(const uint4 (&v)[kQ], uint32_t nchunks, int lane,
+                                               int8_t* xrow, int8_t* qrow, bool write_q) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int u = 0; u < kQ; ++u) amax = absmax_bits8(v[u], amax);
+  amax = wave_max_u32(amax);
+  const float s = row_scale(amax);
+  const bool zero = (amax == 0);
+  const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
+  const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
+#pragma unroll
+  for (int u = 0; u < kQ; ++u) {
+    const uint32_t idx = lane + 64 * u;
+    const uint2 q = quant8(v[u], s, r, zero, exact_div);
+    if (idx < nchunks) {
+      *reinterpret_cast<uint2*>(xrow + 8 * idx) = q;
+      if (write_q) *reinterpret_cast<uint2*>(qrow + 8 * idx) = q;
+    }
+  }
+  return s;
+}
+
+// Rows longer than 64*kQ chunks: an amax pass, then a quantise pass that
+// reads the row again.
+__device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32_t nchunks, int lane,
+                                               int8_t* xrow, int8_t* qrow, bool write_q) {
+  constexpr int U = 8;
+  uint32_t amax = 0;
+  for (uint32_t base = 0; base < nchunks; base += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = load16(rx, (base + lane + 64 * u) * 16u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) amax = absmax_bits8(w[u], amax);
+  }
+  amax = wave_max_u32(amax);
+  const float s = row_scale(amax);
+  const bool zero = (amax == 0);
+  const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
+  const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
+  for (uint32_t base = 0; base < nchunks; base += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = load16(rx, (base + lane + 64 * u) * 16u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + lane + 64 * u;
+      const uint2 q = quant8(w[u], s, r, zero, exact_div);
+      if (idx < nchunks) {
+        *reinterpret_cast<uint2*>(xrow + 8 * idx) = q;
+        if (write_q) *reinterpret_cast<uint2*>(qrow + 8 * idx) = q;
+      }
+    }
+  }
+  return s;
+}
+
+// Three waves per SIMD keep all 576 workgroups of an 18432-row weight
+// resident at once (3 per compute unit).
+template <bool HAS_BIAS, bool TWO, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
+    float* __restrict__ sa_out, int vec_flags) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ float sa_lds[16];
 
@@ -63,133 +146,173 @@ __global__ __launch_bounds__(256) void small_m_kernel(const uint16_t* __restrict
   const int M = (int)a.M;
   const int64_t K = a.K, N = a.N;
   const int ldxs = xs_stride(K);
-  const int64_t n_base = (int64_t)blockIdx.x * 64 + wave * 16;
-  const int rows_valid = (int)max<int64_t>(0, min<int64_t>(16, N - n_base));
+  const int nwin = (int)((K + 127) / 128);
+  const int64_t n_base = (int64_t)blockIdx.x * 32 + wave * 8;
+  const int rows_valid = (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
+  const uint32_t nchunks = (uint32_t)(K >> 3);
+  const bool write_q = blockIdx.x == 0;
 
-  // ---- 0. first weight batches ----
-  const int ksteps = (int)((K + 63) / 64);
-  const int nbatch = (ksteps + kU - 1) / kU;
-  const int frag_row = lane & 15, frag_grp = lane >> 4;
+  // weight windows: lane l reads row l%8, 16-byte chunk l/8 of window w
   const __amdgpu_buffer_rsrc_t rw =
       make_rsrc(a.wq + (rows_valid > 0 ? n_base : 0) * K, (uint32_t)rows_valid * (uint32_t)K);
-  const uint32_t lane_off = (uint32_t)frag_row * (uint32_t)K + 16u * frag_grp;
-  auto load_batch = [&](int bi, v4i* f) {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int kb = (bi * kU + u) * 64 + 16 * frag_grp;     // this lane's K byte
-      const uint32_t off = kb < K ? lane_off + (uint32_t)((bi * kU + u) * 64) : kOOB;
-      f[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
-    }
+  const int chunk = lane >> 3;
+  const uint32_t lane_off = (uint32_t)(lane & 7) * (uint32_t)K + 16u * chunk;
+  auto wload = [&](int w) -> v4i {
+    const bool in = 128 * w + 16 * chunk < K;          // chunks past K read as zero
+    return __builtin_amdgcn_raw_buffer_load_b128(rw, in ? lane_off + 128u * w : kOOB, 0, 0);
   };
-  v4i f[kDepth][kU];
+  v4i buf[kD];
+  auto issue_all = [&]() {
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (d < nbatch) load_batch(d, f[d]);
+    for (int d = 0; d < kD; ++d) buf[d] = wload(d);
+    __builtin_amdgcn_sched_barrier(0);     // all requests out before the first use
+  };
 
-  // ---- 1. activation quantisation into LDS ----
-  // A wave per row; the row is read in batches of kQ x 16 bytes per lane,
-  // all issued together (chunks past K read as zero through the bound).
-  const uint32_t nchunks = (uint32_t)(K >> 3);
-  for (int m = wave; m < M; m += 4) {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2u);
-    uint32_t amax = 0;
-    for (uint32_t base = 0; base < nchunks; base += 64 * kQ) {
-      uint4 v[kQ];
+  // ---- 1. activation quantisation into LDS, 2. weight requests ----
+  // The K tail of each LDS row up to whole windows is never written: it only
+  // meets weights that read as zero. Token rows >= M give unused columns.
+  if constexpr (MODE == ONE_ROW) {
+    uint4 v[kQ];
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)wave * ldx, (uint32_t)K * 2u);
+    if (wave < M) {
 #pragma unroll
-      for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (base + lane + 64 * u) * 16u);
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) amax = absmax_bits8(v[u], amax);
+      for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
     }
-    amax = wave_max_u32(amax);
-    const float s = row_scale(amax);
-    const bool zero = (amax == 0);
-    const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
-    const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
-    for (uint32_t base = 0; base < nchunks; base += 64 * kQ) {
-      uint4 v[kQ];
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (base + lane + 64 * u) * 16u);
-#pragma unroll
-      for (int u = 0; u < kQ; ++u) {
-        const uint32_t idx = base + lane + 64 * u;
-        if (idx < nchunks) {
-          const uint2 q = quant8(v[u], s, r, zero, exact_div);
-          *reinterpret_cast<uint2*>(&xs[m * ldxs + 8 * idx]) = q;
-          if (blockIdx.x == 0) *reinterpret_cast<uint2*>(xq_out + (int64_t)m * K + 8 * idx) = q;
-        }
+    __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0): this wave's row has arrived
+    __syncthreads();                       // ... and every other wave's
+    issue_all();
+    if (wave < M) {
+      const float s = quantise_regs(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
+                                    write_q);
+      if (lane == 0) {
+        sa_lds[wave] = s;
+        if (write_q) sa_out[wave] = s;
       }
     }
-    // the K tail of the row up to whole k-steps is read by the MFMAs against
-    // zero weights; clear it so LDS holds defined values there
-    for (int t = (int)K + 8 * lane; t < ldxs - 16; t += 512)
-      *reinterpret_cast<uint2*>(&xs[m * ldxs + t]) = make_uint2(0u, 0u);
-    if (lane == 0) {
-      sa_lds[m] = s;
-      if (blockIdx.x == 0) sa_out[m] = s;
+    lds_barrier();
+  } else {
+    for (int m = wave; m < M; m += 4) {
+      const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2u);
+      float s;
+      if constexpr (MODE == SHORT) {
+        uint4 v[kQ];
+#pragma unroll
+        for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
+        s = quantise_regs(v, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
+      } else {
+        s = quantise_long(rx, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
+      }
+      if (lane == 0) {
+        sa_lds[m] = s;
+        if (write_q) sa_out[m] = s;
+      }
     }
+    __syncthreads();
+    issue_all();
   }
-  __syncthreads();
   if (rows_valid == 0) return;
 
-  // ---- 2. weight streaming ----
-  v4i acc = v4i{0, 0, 0, 0};
-  const int8_t* xrow = xs + frag_row * ldxs + 16 * frag_grp;
-  auto compute = [&](int bi, const v4i* fb) {
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      // k-steps past the end multiply zero weights; keep the LDS read inside
-      // the row (the last k-step of the padded row)
-      const int ks = min(bi * kU + u, ksteps - 1);
-      const v4i fx = *reinterpret_cast<const v4i*>(xrow + ks * 64);
-      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[u], fx, acc, 0, 0, 0);
+  // ---- 3. weight streaming ----
+  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+  const int8_t* xb = xs + (lane & 7) * ldxs + 16 * chunk;
+  // window w: its LDS read(s) and MFMA(s); windows past the end multiply zero
+  // weights, so the LDS read is kept inside the row (its last window)
+  auto window = [&](int w, const v4i& wv) {
+    const int wc = min(w, nwin - 1);
+    const v4i b0 = *reinterpret_cast<const v4i*>(xb + 128 * wc);
+    acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, b0, acc0, 0, 0, 0);
+    if constexpr (TWO) {
+      const v4i b1 = *reinterpret_cast<const v4i*>(xb + 8 * ldxs + 128 * wc);
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, b1, acc1, 0, 0, 0);
     }
   };
-  int bi = 0;
-  for (; bi + kDepth <= nbatch; bi += kDepth) {
+  if constexpr (MODE != LONG) {
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      compute(bi + d, f[d]);
-      if (bi + d + kDepth < nbatch) load_batch(bi + d + kDepth, f[d]);
+    for (int d = 0; d < kD; ++d) {
+      window(d, buf[d]);
+      __builtin_amdgcn_sched_group_barrier(0x100, TWO ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 1, 0);
+    }
+  } else {
+    for (int base = 0; base < nwin; base += kD) {
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        window(base + d, buf[d]);
+        buf[d] = wload(base + d + kD);
+        __builtin_amdgcn_sched_group_barrier(0x100, TWO ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
     }
   }
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (bi + d < nbatch) compute(bi + d, f[d]);
 
-  // ---- 3. epilogue: lane holds D[n = n_base + 4*(lane/16) + r][m = lane%16] ----
-  const int m = lane & 15;
-  if (m >= M) return;
-  const float sa = sa_lds[m];
-  const int nl = 4 * (lane >> 4);
-  const int64_t n = n_base + nl;
-  uint32_t y[4];
+  // ---- 4. epilogue ----
+  // D[i][j] sits in lane 16*(i/4) + j, element i%4. Row n < 8 at token t < 8
+  // is D[n][t] + D[n+8][t+8], whose second term is 40 lanes up; lanes 0-7
+  // and 16-23 then hold rows nl..nl+3 (nl = 4*(lane/16)) of token lane%8.
+  const int src = ((lane + 40) & 63) * 4;
+  v4i s0, s1;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    if (nl + r < rows_valid) {
-      const float bb = HAS_BIAS ? bf16_to_f32(a.bias[n + r]) : 0.f;
-      y[r] = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(acc[r], sa, a.w_scale[n + r], bb));
-    } else {
-      y[r] = 0;
-    }
+    s0[r] = acc0[r] + __builtin_amdgcn_ds_bpermute(src, acc0[r]);
+    s1[r] = TWO ? acc1[r] + __builtin_amdgcn_ds_bpermute(src, acc1[r]) : 0;
   }
-  uint16_t* o = a.out + (int64_t)m * a.ldo + n;
-  if (nl + 3 < rows_valid && (vec_flags & 1)) {
-    *reinterpret_cast<uint2*>(o) = make_uint2(y[0] | (y[1] << 16), y[2] | (y[3] << 16));
-  } else {
+  if ((lane & 8) != 0 || lane >= 32) return;
+  const int nl = 4 * (lane >> 4);
+  const int64_t n = n_base + nl;
+  float sw[4], bb[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (nl + r < rows_valid) o[r] = (uint16_t)y[r];
+  for (int r = 0; r < 4; ++r) {
+    const bool ok = nl + r < rows_valid;
+    sw[r] = ok ? a.w_scale[n + r] : 0.f;
+    bb[r] = (HAS_BIAS && ok) ? bf16_to_f32(a.bias[n + r]) : 0.f;
   }
-  if (a.acc_debug) {
-    int32_t* dst = a.acc_debug + (int64_t)m * N + n;
-    if (nl + 3 < rows_valid && (vec_flags & 2)) {
-      *reinterpret_cast<int4*>(dst) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+  for (int blk = 0; blk < (TWO ? 2 : 1); ++blk) {
+    const int m = 8 * blk + (lane & 7);
+    if (m >= M) continue;
+    const v4i c = blk ? s1 : s0;
+    const float sa = sa_lds[m];
+    uint32_t y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[r], sa, sw[r], bb[r]));
+    uint16_t* o = a.out + (int64_t)m * a.ldo + n;
+    if (nl + 3 < rows_valid && (vec_flags & 1)) {
+      *reinterpret_cast<uint2*>(o) = make_uint2(y[0] | (y[1] << 16), y[2] | (y[3] << 16));
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (nl + r < rows_valid) dst[r] = acc[r];
+        if (nl + r < rows_valid) o[r] = (uint16_t)y[r];
+    }
+    if (a.acc_debug) {
+      int32_t* dst = a.acc_debug + (int64_t)m * N + n;
+      if (nl + 3 < rows_valid && (vec_flags & 2)) {
+        *reinterpret_cast<int4*>(dst) = make_int4(c[0], c[1], c[2], c[3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (nl + r < rows_valid) dst[r] = c[r];
+      }
     }
   }
+}
+
+template <bool HAS_BIAS, bool TWO>
+hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
+                          float* a_scale_out, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.N + 31) / 32)), block(256);
+  const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)xs_stride(a.K);
+  const int vf = epilogue_vec_flags(a);
+  if (a.K > kShortK)
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, LONG>), grid, block, lds, stream, x, ldx, a,
+                       xq_out, a_scale_out, vf);
+  else if (!TWO && a.M <= 4)
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, false, ONE_ROW>), grid, block, lds, stream, x, ldx,
+                       a, xq_out, a_scale_out, vf);
+  else
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT>), grid, block, lds, stream, x, ldx, a,
+                       xq_out, a_scale_out, vf);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -197,16 +320,11 @@ __global__ __launch_bounds__(256) void small_m_kernel(const uint16_t* __restrict
 hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  const int64_t grid = (a.N + 63) / 64;
-  const size_t lds = (size_t)16 * (size_t)xs_stride(a.K);
-  const int vec_flags = epilogue_vec_flags(a);
   if (a.bias)
-    hipLaunchKernelGGL(small_m_kernel<true>, dim3((unsigned)grid), dim3(256), lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vec_flags);
-  else
-    hipLaunchKernelGGL(small_m_kernel<false>, dim3((unsigned)grid), dim3(256), lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vec_flags);
-  return hipGetLastError();
+    return a.M > 8 ? launch_variant<true, true>(x, ldx, a, xq_out, a_scale_out, stream)
+                   : launch_variant<true, false>(x, ldx, a, xq_out, a_scale_out, stream);
+  return a.M > 8 ? launch_variant<false, true>(x, ldx, a, xq_out, a_scale_out, stream)
+                 : launch_variant<false, false>(x, ldx, a, xq_out, a_scale_out, stream);
 }
 
 }  // namespace w8a8
