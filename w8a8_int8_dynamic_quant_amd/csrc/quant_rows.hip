@@ -4,15 +4,21 @@
 // load-time per-output-channel weight quantisation of the W8A8 int8-dynamic
 // linear (Issue 5 probe, "Round two"; Int8 Quantization guide, "Overview").
 //
-// One wave64 per row, four rows per 256-thread workgroup. Each lane issues
-// all of its 16-byte loads (8 bf16 each) for the row at once, through a
-// buffer descriptor bounded at the row end, so chunks past K read as zero
-// (which leaves amax unchanged) without any branch; a wave reads 1 KiB
-// contiguous per instruction. The row stays in registers between the amax
-// pass and the quantise pass (up to CHUNKS chunks per lane), so x is read
-// from HBM exactly once. amax is an integer max over |x| bit patterns with a
-// DPP butterfly across the wave. Output: 8 int8 per lane and chunk (8-byte
-// buffer stores, 512 B contiguous per wave) and one fp32 scale per row.
+// Rows of up to 4096 elements: one wave per row, every chunk of the row
+// requested at once, all rows in flight together. Longer rows: a workgroup
+// of 4 waves quantises one row at a time and walks over rows
+// blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized so that every
+// workgroup is resident and all do the same number of rows. Thread t holds
+// the row's 16-byte chunks t, t+256, ... (8 bf16 each; 4 KiB contiguous per
+// load instruction of the workgroup) in registers, read through a buffer
+// descriptor bounded at the row end, so chunks past K read as zero (which
+// leaves amax unchanged) without any branch. amax is an integer max over
+// |x| bit patterns: a DPP butterfly within each wave, then the four wave
+// maxima through LDS. While row j is quantised and stored, the loads of row
+// j+1 are already in flight (two register buffers). Output: 8 int8 per
+// chunk (8-byte stores, 2 KiB contiguous per workgroup instruction) and one
+// fp32 scale per row. Rows longer than the register-resident limit use a
+// two-pass kernel (amax pass, then quantise pass re-reading the row).
 #include "w8a8_device.h"
 #include "w8a8_kernels.h"
 
@@ -49,8 +55,72 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-template <int CHUNKS>
+// Barrier on LDS traffic only (lgkmcnt 0, no fence): the loads of the next
+// row and the stores of the previous one stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0); vmcnt and expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int CHT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
+    int8_t* __restrict__ q, float* __restrict__ scale) {
+  __shared__ uint32_t wmax[2][4];          // per-wave amax, one slot per row parity
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t nchunks = (uint32_t)(K >> 3);
+  const int64_t stride = gridDim.x;
+
+  auto load_row = [&](int64_t row, uint4 (&v)[CHT]) {
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * ldx, (uint32_t)K * 2u);
+#pragma unroll
+    for (int u = 0; u < CHT; ++u) v[u] = load16(rx, (uint32_t)(tid + 256 * u) * 16u);
+  };
+  // Quantises row `row` held in `cur`; requests row + stride into `nxt`.
+  auto step = [&](int64_t row, uint4 (&cur)[CHT], uint4 (&nxt)[CHT], int parity) {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int u = 0; u < CHT; ++u) amax = absmax_bits8(cur[u], amax);
+    amax = wave_max_dpp(amax);
+    if ((tid & 63) == 0) wmax[parity][wave] = amax;
+    lds_barrier();
+    if (row + stride < R) load_row(row + stride, nxt);
+    amax = max(max(wmax[parity][0], wmax[parity][1]), max(wmax[parity][2], wmax[parity][3]));
+    const float s = row_scale(amax);
+    const bool zero = (amax == 0);
+    const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;  // subnormal s
+    const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
+    const __amdgpu_buffer_rsrc_t rq = row_rsrc(q + row * K, (uint32_t)K);
+#pragma unroll
+    for (int u = 0; u < CHT; ++u) {
+      const uint32_t idx = (uint32_t)(tid + 256 * u);
+      store8(quant8(cur[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
+    }
+    if (tid == 0) scale[row] = s;
+  };
+
+  int64_t row = blockIdx.x;
+  if (row >= R) return;
+  uint4 va[CHT], vb[CHT];
+  load_row(row, va);
+  for (;;) {
+    step(row, va, vb, 0);
+    row += stride;
+    if (row >= R) break;
+    step(row, vb, va, 1);
+    row += stride;
+    if (row >= R) break;
+  }
+}
+
+// Short rows: one wave per row, four rows per workgroup, every chunk of the
+// row (CHUNKS per lane) requested at once and kept in registers between the
+// amax and the quantise step; all rows are in flight together.
+template <int CHUNKS>
+__global__ __launch_bounds__(256) void quant_rows_wave_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
@@ -60,7 +130,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const uint32_t nchunks = (uint32_t)(K >> 3);
   const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + row * ldx, (uint32_t)K * 2u);
   const __amdgpu_buffer_rsrc_t rq = row_rsrc(q + row * K, (uint32_t)K);
-
   uint4 v[CHUNKS];
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) v[c] = load16(rx, (uint32_t)(lane + 64 * c) * 16u);
@@ -80,8 +149,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   if (lane == 0) scale[row] = s;
 }
 
-// Rows longer than the register-resident limit: amax pass, then a second
-// pass that re-reads the row (from L2 for the row lengths that get here).
+// Rows longer than the register-resident limit: one wave per row, an amax
+// pass, then a second pass that re-reads the row (from L2 for the row
+// lengths that get here).
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -118,6 +188,29 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
   if (lane == 0) scale[row] = s;
 }
 
+// Workgroups of `kernel` (256 threads) the current device holds at once.
+int resident_workgroups(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 1024;
+  return cus * per_cu;
+}
+
+template <int C>
+hipError_t launch_cht(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, int8_t* q, float* scale,
+                      hipStream_t stream) {
+  static int resident = 0;               // per kernel; the same value on every device here
+  if (resident == 0) resident = resident_workgroups((const void*)quant_rows_kernel<C>);
+  // as many resident workgroups as possible, each doing the same row count
+  const int64_t rows_per_wg = (R + resident - 1) / resident;
+  const dim3 grid((unsigned)((R + rows_per_wg - 1) / rows_per_wg)), block(256);
+  hipLaunchKernelGGL(quant_rows_kernel<C>, grid, block, 0, stream, x, R, K, ldx, q, scale);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ldx,
@@ -125,23 +218,29 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ld
   if (R == 0) return hipSuccess;
   const int64_t nchunks = K >> 3;
   const int64_t per_lane = (nchunks + 63) / 64;
-  dim3 grid((unsigned)((R + 3) / 4)), block(256);
-#define W8A8_QR(C)                                                                     \
-  if (per_lane <= C) {                                                                 \
-    hipLaunchKernelGGL(quant_rows_kernel<C>, grid, block, 0, stream, x, R, K, ldx, q, scale); \
-    return hipGetLastError();                                                          \
+  if (per_lane <= 8) {                    // K <= 4096: a wave per row
+    const dim3 grid((unsigned)((R + 3) / 4)), block(256);
+#define W8A8_QW(C)                                                                        \
+    if (per_lane <= C) {                                                                  \
+      hipLaunchKernelGGL(quant_rows_wave_kernel<C>, grid, block, 0, stream, x, R, K, ldx, q, \
+                         scale);                                                          \
+      return hipGetLastError();                                                           \
+    }
+    W8A8_QW(1)
+    W8A8_QW(2)
+    W8A8_QW(4)
+    W8A8_QW(6)
+    W8A8_QW(8)
+#undef W8A8_QW
   }
-  W8A8_QR(1)
-  W8A8_QR(2)
-  W8A8_QR(4)
-  W8A8_QR(6)
-  W8A8_QR(8)
-  W8A8_QR(12)
-  W8A8_QR(16)
-  W8A8_QR(24)
-  W8A8_QR(32)
-#undef W8A8_QR
-  hipLaunchKernelGGL(quant_rows_long_kernel, grid, block, 0, stream, x, R, K, ldx, q, scale);
+  const int64_t per_thread = (nchunks + 255) / 256;
+  if (per_thread <= 4) return launch_cht<4>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 6) return launch_cht<6>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 8) return launch_cht<8>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 12) return launch_cht<12>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 16) return launch_cht<16>(x, R, K, ldx, q, scale, stream);
+  hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, x, R,
+                     K, ldx, q, scale);
   return hipGetLastError();
 }
 
