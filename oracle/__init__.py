@@ -23,4 +23,6 @@ from .w8a8_oracle import (  # noqa: F401
     float_reference,
     noise_model_rel_l2,
     rel_l2,
+    unpack_pack_quantized,
+    scale_to_f32,
 )

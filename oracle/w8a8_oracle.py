@@ -241,3 +241,38 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+# --------------------------------------------------------------------------
+# compressed-tensors pack-quantized ingest
+#
+# "Issue 5 probe ...", section "Round one: int8 weight-only via
+# compressed-tensors": the int8 weight-only checkpoint stores its weights with
+# compressed-tensors' pack_to_int32, as uint8 biased by 128, four per int32,
+# with a per-output-channel scale.
+# Readings where the page is silent: element 4i+j of a row sits in bits
+# 8j..8j+7 of word i (little-endian, first element in the low byte); the int8
+# value is the stored byte minus 128; the scale converts to fp32 exactly from
+# fp32, bf16 or fp16.
+
+def unpack_pack_quantized(packed_words) -> np.ndarray:
+    """int32 words [N, W] -> int8 [N, 4W]: q[n, 4i+j] = ((word >> 8j) & 0xFF) - 128."""
+    w = np.asarray(packed_words).astype(np.int64) & 0xFFFFFFFF
+    N, W = w.shape
+    q = np.empty((N, 4 * W), np.int16)
+    for j in range(4):
+        q[:, j::4] = ((w >> (8 * j)) & 0xFF) - 128
+    return q.astype(np.int8)
+
+
+def scale_to_f32(scale, dtype: str) -> np.ndarray:
+    """Per-channel scale as fp32: dtype 'f32' (values), 'bf16' or 'f16' (bit patterns)."""
+    a = np.asarray(scale)
+    if dtype == "f32":
+        return a.astype(np.float32)
+    if dtype == "bf16":
+        return bf16_bits_to_f32(a.astype(np.uint16))
+    if dtype == "f16":
+        return a.astype(np.uint16).view(np.float16).astype(np.float32)
+    raise ValueError(dtype)
+

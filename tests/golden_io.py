@@ -47,3 +47,12 @@ def gemm_case():
         tag, *vals = line.split()
         rows[tag].append([int(v) for v in vals])
     return rows["xq"], rows["wq"], rows["acc"]
+
+
+def pack_quantized_cases():
+    """[(word as unsigned int, [four int8 values])]"""
+    out = []
+    for line in _lines("pack_quantized_hand_cases.txt"):
+        w, qs = (p.strip() for p in line.split("|"))
+        out.append((int(w, 16), [int(t) for t in qs.split()]))
+    return out
