@@ -130,6 +130,30 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 
 #define W8A8_ALIGN256(b) ((((size_t)(b)) + 255u) & ~(size_t)255u)
 
+/*
+ * compressed-tensors pack-quantized ingest (Issue 5 probe, "Round one: int8
+ * weight-only via compressed-tensors": weights stored with pack_to_int32, as
+ * uint8 biased by 128, four per int32).
+ *   packed   [N, ldp] int32 (read); element 4i+j of a row is bits 8j..8j+7 of
+ *            word i (little-endian), stored as q + 128
+ *   scale_in [N] per-output-channel scale, type scale_dtype (W8A8_SCALE_F32,
+ *            W8A8_SCALE_BF16 or W8A8_SCALE_F16) (read)
+ *   wq       [N, K] int8, row stride K (written): q = stored byte - 128
+ *   w_scale  [N] fp32 (written; every input type converts exactly)
+ * The result feeds w8a8_linear / w8a8_scaled_mm like the output of
+ * w8a8_quantize_weights. Requirements: 16 <= K <= W8A8_K_MAX, K % 16 == 0,
+ * ldp >= K/4 and ldp % 4 == 0 (else W8A8_ERR_UNSUPPORTED / INVALID_ARG);
+ * packed and wq 16-byte aligned. A stored byte 0 gives q = -128, which the
+ * symmetric quantiser never produces; with such weights the int32-safe K is
+ * 132 104 (127 * 128 * K < 2^31) rather than W8A8_K_MAX.
+ */
+#define W8A8_SCALE_F32 0
+#define W8A8_SCALE_BF16 1
+#define W8A8_SCALE_F16 2
+int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int64_t ldp,
+                               const void* scale_in, int scale_dtype, int8_t* wq,
+                               float* w_scale, void* stream);
+
 /* Workspace bytes w8a8_linear needs for this shape (0 if M == 0). */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

@@ -135,6 +135,35 @@ def test_workspace_and_path_queries():
     assert bm >= 128 and bn >= 128
 
 
+def test_unpack_validation():
+    f = "w8a8_unpack_pack_quantized"
+    base = [P(A), 8, 64, 16, P(A), w8.SCALE_F32, P(A), P(A), None]
+    names = ["packed", "N", "K", "ldp", "scale", "dtype", "wq", "ws", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(N=-1) == w8.ERR_INVALID_ARG
+    assert call(K=40) == w8.ERR_UNSUPPORTED
+    assert call(K=0) == w8.ERR_UNSUPPORTED
+    assert call(ldp=15) == w8.ERR_INVALID_ARG            # ldp < K/4
+    assert call(ldp=18) == w8.ERR_UNSUPPORTED            # ldp % 4
+    assert call(dtype=3) == w8.ERR_INVALID_ARG
+    assert call(packed=None) == w8.ERR_INVALID_ARG
+    assert call(scale=None) == w8.ERR_INVALID_ARG
+    assert call(wq=None) == w8.ERR_INVALID_ARG
+    assert call(ws=None) == w8.ERR_INVALID_ARG
+    assert call(packed=P(A + 4)) == w8.ERR_MISALIGNED
+    assert call(wq=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(ws=P(A + 2)) == w8.ERR_MISALIGNED
+    assert call(scale=P(A + 2)) == w8.ERR_MISALIGNED     # fp32 scales need 4 bytes
+    assert call(N=0, packed=None, scale=None, wq=None, ws=None) == w8.OK
+    assert f"#define W8A8_SCALE_BF16 {w8.SCALE_BF16}" in open(HEADER).read()
+
+
 def test_status_strings():
     for s in (w8.OK, w8.ERR_INVALID_ARG, w8.ERR_UNSUPPORTED, w8.ERR_MISALIGNED,
               w8.ERR_WORKSPACE, w8.ERR_HIP):

@@ -10,6 +10,7 @@ there is no fallback.
     y = linear(x, wq, w_scale, bias)               # bf16 [M, K] -> bf16 [M, N]
     xq, a_scale = quant_act(x)                     # the two ops separately
     y = scaled_mm(xq, a_scale, wq, w_scale, bias)
+    wq, w_scale = unpack_pack_quantized(packed, scale)  # compressed-tensors ingest
 """
 from __future__ import annotations
 
@@ -30,6 +31,7 @@ ERR_HIP = -5
 K_MAX = 133144
 SMALL_M = 16
 PATH_NONE, PATH_SMALL_M, PATH_GEMM = 0, 1, 2
+SCALE_F32, SCALE_BF16, SCALE_F16 = 0, 1, 2
 
 SYMBOLS = (
     "w8a8_quantize_weights",
@@ -39,6 +41,7 @@ SYMBOLS = (
     "w8a8_linear_workspace_bytes",
     "w8a8_linear_path",
     "w8a8_gemm_tile",
+    "w8a8_unpack_pack_quantized",
     "w8a8_status_string",
     "w8a8_last_hip_error",
 )
@@ -75,11 +78,13 @@ def lib() -> ctypes.CDLL:
     L.w8a8_linear_workspace_bytes.restype = sz
     L.w8a8_linear_path.argtypes = [i64, i64, i64]
     L.w8a8_gemm_tile.argtypes = [i64, i64, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
+    L.w8a8_unpack_pack_quantized.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
     L.w8a8_status_string.argtypes = [ci]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for name in ("w8a8_quantize_weights", "w8a8_quant_act", "w8a8_scaled_mm", "w8a8_linear",
-                 "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_last_hip_error"):
+                 "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized",
+                 "w8a8_last_hip_error"):
         getattr(L, name).restype = ci
     _lib = L
     return L
@@ -175,6 +180,31 @@ def scaled_mm(xq, a_scale, wq, w_scale, bias=None, out=None, acc_debug=None):
                                 _ptr(bias), _ptr(out), ldo, _ptr(acc_debug),
                                 _stream(xq.device)))
     return out
+
+
+_SCALE_DTYPES = {torch.float32: SCALE_F32, torch.bfloat16: SCALE_BF16, torch.float16: SCALE_F16}
+
+
+def unpack_pack_quantized(packed: torch.Tensor, scale: torch.Tensor):
+    """compressed-tensors pack-quantized weights -> (wq int8 [N, K], w_scale fp32 [N]).
+
+    packed: int32 [N, K/4] (uint8 biased by 128, four per word, little-endian);
+    scale: fp32, bf16 or fp16 of N elements ([N] or [N, 1]).
+    """
+    N, words, ldp = _rows(packed, torch.int32, "packed")
+    K = 4 * words
+    if scale.dtype not in _SCALE_DTYPES or scale.numel() != N or not scale.is_cuda:
+        raise ValueError("scale must be a fp32/bf16/fp16 GPU tensor of N elements")
+    scale = scale.reshape(N)
+    if not scale.is_contiguous():
+        raise ValueError("scale must be contiguous")
+    wq = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    s = torch.empty((N,), dtype=torch.float32, device=packed.device)
+    _check("w8a8_unpack_pack_quantized",
+           lib().w8a8_unpack_pack_quantized(_ptr(packed), N, K, ldp, _ptr(scale),
+                                            _SCALE_DTYPES[scale.dtype], _ptr(wq), _ptr(s),
+                                            _stream(packed.device)))
+    return wq, s
 
 
 def workspace_bytes(M: int, K: int, N: int) -> int:

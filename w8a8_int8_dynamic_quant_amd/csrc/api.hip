@@ -126,6 +126,25 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8
   return hip_status(w8a8::launch_gemm(g, st));
 }
 
+int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int64_t ldp,
+                               const void* scale_in, int scale_dtype, int8_t* wq, float* w_scale,
+                               void* stream) {
+  if (N < 0) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(K)) return s;
+  if (ldp < K / 4) return W8A8_ERR_INVALID_ARG;
+  if (ldp % 4 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (scale_dtype != W8A8_SCALE_F32 && scale_dtype != W8A8_SCALE_BF16 &&
+      scale_dtype != W8A8_SCALE_F16)
+    return W8A8_ERR_INVALID_ARG;
+  if (N == 0) return W8A8_OK;
+  if (!packed || !scale_in || !wq || !w_scale) return W8A8_ERR_INVALID_ARG;
+  const uintptr_t salign = scale_dtype == W8A8_SCALE_F32 ? 4 : 2;
+  if (!aligned(packed, 16) || !aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(scale_in, salign))
+    return W8A8_ERR_MISALIGNED;
+  return hip_status(w8a8::launch_unpack(packed, N, K, ldp, scale_in, scale_dtype, wq, w_scale,
+                                        (hipStream_t)stream));
+}
+
 const char* w8a8_status_string(int status) {
   switch (status) {
     case W8A8_OK: return "ok";
