@@ -25,4 +25,7 @@ from .w8a8_oracle import (  # noqa: F401
     rel_l2,
     unpack_pack_quantized,
     scale_to_f32,
+    w8a16_acc,
+    w8a16_abs_sum,
+    w8a16_linear,
 )

@@ -276,3 +276,43 @@ def scale_to_f32(scale, dtype: str) -> np.ndarray:
         return a.astype(np.uint16).view(np.float16).astype(np.float32)
     raise ValueError(dtype)
 
+
+# --------------------------------------------------------------------------
+# W8A16: int8 weight-only with bf16 activations
+#
+# "Issue 5 probe ...", section "Round one: int8 weight-only via
+# compressed-tensors": int8 weight-only (W8A16), per-output-channel symmetric
+# weights, bf16 activations (no activation quantisation).
+# Readings where the page is silent: the per-channel scale is applied once
+# to the sum, acc = sum_k fp32(x[k]) * wq[n,k] (each product is exact in
+# fp32: 8 x 8 significant bits), y = bf16_rne(fl32(fl32(acc) * s_w) +
+# fp32(bias)); the oracle takes acc in float64 (exact for inputs whose
+# products span fewer than 53 bits) and rounds it to fp32 once. A kernel that
+# accumulates in fp32 differs from it by its accumulation error, bounded in
+# the parity test by a multiple of 2^-24 * sum_k |x[k] * wq[n,k]|.
+
+def w8a16_acc(x_bits, wq) -> np.ndarray:
+    """float64 sum_k x[m,k] * wq[n,k] for bf16 x [M,K] and int8 wq [N,K]."""
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    return x @ np.asarray(wq, np.float64).T
+
+
+def w8a16_abs_sum(x_bits, wq) -> np.ndarray:
+    """sum_k |x[m,k] * wq[n,k]|, the scale of the accumulation error."""
+    x = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
+    return x @ np.abs(np.asarray(wq, np.float64)).T
+
+
+def w8a16_linear(x_bits, wq, s_w, bias_bits=None) -> dict:
+    """W8A16 linear: bf16 x [M,K], int8 wq [N,K], fp32 s_w [N] -> bf16 y bits.
+
+    Returns acc (float64) and y (bf16 bits).
+    """
+    acc = w8a16_acc(x_bits, wq)
+    t = acc.astype(np.float32)                                   # one RNE rounding
+    t = t * np.asarray(s_w, dtype=np.float32)[None, :]
+    if bias_bits is not None:
+        t = t + bf16_bits_to_f32(bias_bits)[None, :]
+    assert t.dtype == np.float32
+    return {"acc": acc, "y": f32_to_bf16_bits(t)}
+

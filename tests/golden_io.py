@@ -56,3 +56,13 @@ def pack_quantized_cases():
         w, qs = (p.strip() for p in line.split("|"))
         out.append((int(w, 16), [int(t) for t in qs.split()]))
     return out
+
+
+def w8a16_cases():
+    """[(x values, wq values, s_w, bias_bits or None, y_bits)]"""
+    out = []
+    for line in _lines("w8a16_hand_cases.txt"):
+        xs, ws, s, b, y = (p.strip() for p in line.split("|"))
+        out.append(([_num(t) for t in xs.split()], [int(t) for t in ws.split()], _num(s),
+                    None if b == "-" else int(b, 16), int(y, 16)))
+    return out
