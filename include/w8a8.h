@@ -154,6 +154,25 @@ int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int6
                                const void* scale_in, int scale_dtype, int8_t* wq,
                                float* w_scale, void* stream);
 
+/*
+ * W8A16 linear for small M: int8 weight-only with bf16 activations, no
+ * activation quantisation (Issue 5 probe, "Round one: int8 weight-only via
+ * compressed-tensors": per-output-channel symmetric int8 weights, bf16
+ * activations), for the M <= 16 layers that stream their weight once.
+ *   x [M, ldx] bf16; wq [N, K] int8 (row stride K); w_scale [N] fp32
+ *   (from w8a8_quantize_weights or w8a8_unpack_pack_quantized);
+ *   bias [N] bf16 or NULL; out [M, ldo] bf16 (written)
+ *   acc[m,n] = sum_k fp32(x[m,k]) * wq[n,k]   (fp32 accumulation, MFMA order)
+ *   y[m,n]   = bf16_rne(fl32(acc * w_scale[n]) + bias[n])
+ * Requirements as w8a8_linear, plus M <= W8A16_MAX_M and K small enough that
+ * the activations fit on chip: K <= 8064 for M <= 8, K <= 3968 for M <= 16
+ * (else W8A8_ERR_UNSUPPORTED). No workspace.
+ */
+#define W8A16_MAX_M 16
+int w8a16_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                 const int8_t* wq, const float* w_scale, int64_t N,
+                 const uint16_t* bias, uint16_t* out, int64_t ldo, void* stream);
+
 /* Workspace bytes w8a8_linear needs for this shape (0 if M == 0). */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

@@ -19,7 +19,7 @@ A = 0x10000          # a fake, 256-byte aligned device address (never dereferenc
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(w8a8_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(w8a(?:8|16)_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_binding_symbols():
@@ -162,6 +162,32 @@ def test_unpack_validation():
     assert call(scale=P(A + 2)) == w8.ERR_MISALIGNED     # fp32 scales need 4 bytes
     assert call(N=0, packed=None, scale=None, wq=None, ws=None) == w8.OK
     assert f"#define W8A8_SCALE_BF16 {w8.SCALE_BF16}" in open(HEADER).read()
+
+
+def test_w8a16_validation():
+    f = "w8a16_linear"
+    base = [P(A), 4, 3072, 3072, P(A), P(A), 64, None, P(A), 64, None]
+    names = ["x", "M", "K", "ldx", "wq", "sw", "N", "bias", "out", "ldo", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(M=-1) == w8.ERR_INVALID_ARG
+    assert call(M=17) == w8.ERR_UNSUPPORTED                   # small-M path only
+    assert call(M=16, K=3984, ldx=3984) == w8.ERR_UNSUPPORTED   # activations exceed LDS
+    assert call(M=8, K=8080, ldx=8080) == w8.ERR_UNSUPPORTED
+    assert call(K=40, ldx=40) == w8.ERR_UNSUPPORTED
+    assert call(ldx=3000) == w8.ERR_INVALID_ARG
+    assert call(ldx=3076) == w8.ERR_UNSUPPORTED
+    assert call(x=None) == w8.ERR_INVALID_ARG
+    assert call(wq=None) == w8.ERR_INVALID_ARG
+    assert call(x=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(bias=P(A + 1)) == w8.ERR_MISALIGNED
+    assert call(M=0, x=None) == w8.OK
+    assert f"#define W8A16_MAX_M {w8.W8A16_MAX_M}" in open(HEADER).read()
 
 
 def test_status_strings():

@@ -11,6 +11,7 @@ there is no fallback.
     xq, a_scale = quant_act(x)                     # the two ops separately
     y = scaled_mm(xq, a_scale, wq, w_scale, bias)
     wq, w_scale = unpack_pack_quantized(packed, scale)  # compressed-tensors ingest
+    y = w8a16_linear(x, wq, w_scale, bias)         # weight-only, M <= 16
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ K_MAX = 133144
 SMALL_M = 16
 PATH_NONE, PATH_SMALL_M, PATH_GEMM = 0, 1, 2
 SCALE_F32, SCALE_BF16, SCALE_F16 = 0, 1, 2
+W8A16_MAX_M = 16
 
 SYMBOLS = (
     "w8a8_quantize_weights",
@@ -42,6 +44,7 @@ SYMBOLS = (
     "w8a8_linear_path",
     "w8a8_gemm_tile",
     "w8a8_unpack_pack_quantized",
+    "w8a16_linear",
     "w8a8_status_string",
     "w8a8_last_hip_error",
 )
@@ -79,11 +82,12 @@ def lib() -> ctypes.CDLL:
     L.w8a8_linear_path.argtypes = [i64, i64, i64]
     L.w8a8_gemm_tile.argtypes = [i64, i64, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.w8a8_unpack_pack_quantized.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
+    L.w8a16_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp]
     L.w8a8_status_string.argtypes = [ci]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for name in ("w8a8_quantize_weights", "w8a8_quant_act", "w8a8_scaled_mm", "w8a8_linear",
-                 "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized",
+                 "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized", "w8a16_linear",
                  "w8a8_last_hip_error"):
         getattr(L, name).restype = ci
     _lib = L
@@ -205,6 +209,26 @@ def unpack_pack_quantized(packed: torch.Tensor, scale: torch.Tensor):
                                             _SCALE_DTYPES[scale.dtype], _ptr(wq), _ptr(s),
                                             _stream(packed.device)))
     return wq, s
+
+
+def w8a16_linear(x, wq, w_scale, bias=None, out=None):
+    """W8A16 linear for M <= 16: bf16 x [M, K] (not quantised) with int8
+    weights [N, K] and fp32 per-channel scales -> bf16 [M, N]."""
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    N, K2, ldw = _rows(wq, torch.int8, "wq")
+    if K2 != K or (N > 1 and ldw != K):
+        raise ValueError("wq must be contiguous [N, K] with the K of x")
+    _vec(w_scale, torch.float32, N, "w_scale")
+    _vec(bias, torch.bfloat16, N, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    Mo, No, ldo = _rows(out, torch.bfloat16, "out")
+    if (Mo, No) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check("w8a16_linear",
+           lib().w8a16_linear(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(out),
+                              ldo, _stream(x.device)))
+    return out
 
 
 def workspace_bytes(M: int, K: int, N: int) -> int:

@@ -60,4 +60,11 @@ constexpr int kScaleF32 = 0, kScaleBF16 = 1, kScaleF16 = 2;
 hipError_t launch_unpack(const int32_t* packed, int64_t N, int64_t K, int64_t ldp, const void* scale_in,
                          int scale_dtype, int8_t* wq, float* w_scale, hipStream_t stream);
 
+// W8A16 small-M linear: bf16 x [M, ldx] (M <= 16), int8 wq, fp32 w_scale,
+// fp32 accumulation, bf16 out. a.xq / a.a_scale / a.acc_debug are unused.
+// Needs w8a16_lds_bytes(M, K) <= kW8A16MaxLds bytes of LDS.
+constexpr size_t kW8A16MaxLds = 128 * 1024;
+size_t w8a16_lds_bytes(int64_t M, int64_t K);
+hipError_t launch_w8a16(const uint16_t* x, int64_t ldx, const GemmArgs& a, hipStream_t stream);
+
 }  // namespace w8a8
