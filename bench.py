@@ -62,10 +62,15 @@ def copy_calibration(mib: int) -> None:
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
 
 
+# The sources the GEMM kernel is compiled from (its file and the headers it
+# includes); the committed HBM counters stay valid while these are unchanged.
+GEMM_SOURCES = ("gemm_i8.hip", "w8a8_device.h", "w8a8_kernels.h")
+
+
 def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "w8a8_int8_dynamic_quant_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
+    for f in GEMM_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -120,6 +125,79 @@ def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
         "cpu_model": platform.processor() or platform.machine(),
         "numpy": np.__version__,
     }
+
+
+def next_rows(w8, torch, np, dev, to_dev) -> dict:
+    """The layers beyond the block step, measured after it on their own.
+
+    Modulation projection 3072->18432 at M = 1, 8, 16 with bias: W8A16
+    (bf16 activations, int8 weights) against the W8A8 small-M kernel, both
+    HBM-bound (the weight is read once), reported as algorithmic GB/s =
+    (2MK + NK + 4N + 2N + 2MN) / t. Pack-quantized ingest of the same weight
+    (N*K/4 words in, N*K int8 + N fp32 out). Each figure is the median over 5
+    batches of 60 back-to-back calls bracketed by HIP events, rotating over
+    copies of the weight that together exceed the 256 MB last-level cache.
+    """
+    from synth_inputs import make_linear_inputs
+    lib = w8.lib()
+    sp = torch.cuda.current_stream(dev)
+    d = make_linear_inputs("mod_m16_3072x18432")
+    K, N = d["K"], d["N"]
+    n_copies = 10
+    wq0, sw = w8.quantize_weights(to_dev(d["w"]))
+    wqs = [wq0] + [wq0.clone() for _ in range(n_copies - 1)]
+    bias, x = to_dev(d["bias"]), to_dev(d["x"])
+    out = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((w8.workspace_bytes(16, K, N),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def timed(fn, calls=60, batches=5):
+        for i in range(10):
+            fn(i)
+        per_call = []
+        for _ in range(batches):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(sp)
+            for i in range(calls):
+                fn(i)
+            e1.record(sp)
+            e1.synchronize()
+            per_call.append(e0.elapsed_time(e1) / calls)
+        return float(np.median(per_call)) * 1e3
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(f"libw8a8 status {st}")
+
+    res = {"shape": f"Mx{K}x{N}, bias", "modulation": {}}
+    for M in (1, 8, 16):
+        alg = 2 * M * K + N * K + 4 * N + 2 * N + 2 * M * N
+        us16 = timed(lambda i: ok(lib.w8a16_linear(
+            x.data_ptr(), M, K, K, wqs[i % n_copies].data_ptr(), sw.data_ptr(), N,
+            bias.data_ptr(), out.data_ptr(), N, sp.cuda_stream)))
+        us8 = timed(lambda i: ok(lib.w8a8_linear(
+            x.data_ptr(), M, K, K, wqs[i % n_copies].data_ptr(), sw.data_ptr(), N,
+            bias.data_ptr(), out.data_ptr(), N, ws.data_ptr(), ws.numel(), None,
+            sp.cuda_stream)))
+        res["modulation"][f"M{M}"] = {
+            "w8a16_us": us16, "w8a16_gbs": alg / (us16 * 1e-6) / 1e9,
+            "w8a16_pct_hbm": 100 * alg / (us16 * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "w8a8_us": us8, "w8a8_gbs": alg / (us8 * 1e-6) / 1e9,
+            "w8a8_pct_hbm": 100 * alg / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    del wqs
+    n_pk = 5
+    packed0 = (wq0.to(torch.int16) + 128).to(torch.uint8).view(torch.int32)
+    packs = [packed0] + [packed0.clone() for _ in range(n_pk - 1)]
+    outs = [torch.empty_like(wq0) for _ in range(n_pk)]
+    s_out = torch.empty_like(sw)
+    torch.cuda.synchronize()
+    us = timed(lambda i: ok(lib.w8a8_unpack_pack_quantized(
+        packs[i % n_pk].data_ptr(), N, K, K // 4, sw.data_ptr(), w8.SCALE_F32,
+        outs[i % n_pk].data_ptr(), s_out.data_ptr(), sp.cuda_stream)))
+    alg = 2 * N * K + 8 * N
+    res["unpack_pack_quantized"] = {"us": us, "gbs": alg / (us * 1e-6) / 1e9,
+                                    "pct_hbm": 100 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return res
 
 
 def main():
@@ -305,6 +383,8 @@ def main():
                            f"{n_bd}-step pass after the timed region; gemm_us/gemm_tops and "
                            "roofline: events around the GEMM launches inside the timed region"),
     }
+    print("[bench] next rows (W8A16, ingest)", file=sys.stderr, flush=True)
+    line["next_rows"] = next_rows(w8, torch, np, dev, to_dev)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         import oracle
