@@ -6,15 +6,17 @@
 // test_diffusion_transformer_quant.py). Here they are served by a kernel
 // whose cost is streaming the int8 weight once from HBM.
 //
-// Workgroup of 4 waves, 32 weight rows; each wave owns 8 rows over the whole
-// K, read in 128-byte windows:
+// Workgroups of W waves (4..12, one workgroup per CU when the weight allows;
+// see row_groups.h), each wave owning 8 weight rows over the whole K, read in
+// 128-byte windows:
 //  1. the M activation rows are quantised on chip (per-row amax, scale =
 //     amax/127, exact half-to-even rounding) into LDS as int8 [M][K];
 //     workgroup 0 also writes xq and a_scale out for the caller. The rows
 //     are read before any weight window is requested: vector-memory requests
 //     of the whole chip share the same queues, and the few KiB of x requested
-//     behind the weight stream would arrive last. With M <= 4 (one row per
-//     wave) the quantisation itself then runs while the weights stream;
+//     behind the weight stream would arrive last. With M <= W (at most one
+//     row per wave) the quantisation itself then runs while the weights
+//     stream;
 //  2. the wave requests up to kD 128-byte windows of its rows at once
 //     (one buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte
 //     chunk l/8, so every instruction fetches 8 whole 128-byte lines).
@@ -29,6 +31,7 @@
 //     wave's rows, so rows past N and chunks past K read as zero, branch-free;
 //  3. the epilogue is the GEMM's, in the same fp32 order, so a row gives
 //     bit-identical results on either path.
+#include "row_groups.h"
 #include "w8a8_device.h"
 #include "w8a8_kernels.h"
 
@@ -41,7 +44,7 @@ constexpr int kD = 24;                   // 128-byte windows in flight per wave
 constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisation batch
 constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
 
-// Work split of a launch: ONE_ROW: M <= 4 and K <= kShortK (a wave quantises
+// Work split of a launch: ONE_ROW: M <= W and K <= kShortK (a wave quantises
 // at most one activation row, overlapped with the weight stream); SHORT:
 // K <= kShortK; LONG: longer rows (read twice for quantisation, weight
 // windows refilled as they are consumed).
@@ -132,10 +135,9 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
   return s;
 }
 
-// Three waves per SIMD keep all 576 workgroups of an 18432-row weight
-// resident at once (3 per compute unit).
+// Up to kMaxWaves waves per workgroup: three waves per SIMD.
 template <bool HAS_BIAS, bool TWO, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
+__global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
     float* __restrict__ sa_out, int vec_flags) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
@@ -143,11 +145,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
   const int M = (int)a.M;
   const int64_t K = a.K, N = a.N;
   const int ldxs = xs_stride(K);
   const int nwin = (int)((K + 127) / 128);
-  const int64_t n_base = (int64_t)blockIdx.x * 32 + wave * 8;
+  const int64_t n_base = ((int64_t)blockIdx.x * W + wave) * 8;
   const int rows_valid = (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
   const uint32_t nchunks = (uint32_t)(K >> 3);
   const bool write_q = blockIdx.x == 0;
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     }
     lds_barrier();
   } else {
-    for (int m = wave; m < M; m += 4) {
+    for (int m = wave; m < M; m += W) {
       const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2u);
       float s;
       if constexpr (MODE == SHORT) {
@@ -300,14 +303,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 template <bool HAS_BIAS, bool TWO>
 hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.N + 31) / 32)), block(256);
+  const RowGroupGrid g = row_group_grid(a.N);
+  const dim3 grid(g.blocks), block(64 * g.waves);
   const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)xs_stride(a.K);
   const int vf = epilogue_vec_flags(a);
   if (a.K > kShortK)
     hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, LONG>), grid, block, lds, stream, x, ldx, a,
                        xq_out, a_scale_out, vf);
-  else if (!TWO && a.M <= 4)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, false, ONE_ROW>), grid, block, lds, stream, x, ldx,
+  else if (a.M <= g.waves)
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, ONE_ROW>), grid, block, lds, stream, x, ldx,
                        a, xq_out, a_scale_out, vf);
   else
     hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT>), grid, block, lds, stream, x, ldx, a,

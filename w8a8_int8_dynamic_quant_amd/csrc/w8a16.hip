@@ -9,8 +9,9 @@
 // Every bf16 x int8 product is exact in fp32; the accumulation order is the
 // MFMA's.
 //
-// Workgroup of 4 waves, 32 weight rows, each wave 8 rows over all of K in
-// 128-byte windows, as the W8A8 small-M kernel:
+// Workgroups of W waves (4..12, one workgroup per CU when the weight allows;
+// see row_groups.h), each wave 8 weight rows over all of K in 128-byte
+// windows, as the W8A8 small-M kernel:
 //  1. the M activation rows are copied into LDS as bf16 by LDS-DMA
 //     (buffer_load ... lds) before any weight window is requested; chunks
 //     past K read as zero through the descriptor bound, so the padded tail
@@ -23,6 +24,7 @@
 //     weight row i%8 at chunk parity i/8 (B built the same way from LDS), so
 //     D[n][t] + D[n+8][t+8] is the dot product of row n and token t;
 //  3. epilogue in fp32: (acc * s_w) + bias, bf16 round to nearest even.
+#include "row_groups.h"
 #include "w8a8_device.h"
 #include "w8a8_kernels.h"
 
@@ -69,16 +71,17 @@ __device__ __forceinline__ v8bf widen8(uint32_t lo, uint32_t hi) {
 }
 
 template <bool HAS_BIAS, bool TWO, bool LONG>
-__global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+__global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                     GemmArgs a, int vec_flags) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int W = blockDim.x >> 6;
   const int M = (int)a.M;
   const int64_t K = a.K, N = a.N;
   const int row_bytes = w8a16_row_bytes(K);
   const int nwin = (int)((K + 127) / 128);
-  const int64_t n_base = (int64_t)blockIdx.x * 32 + wave * 8;
+  const int64_t n_base = ((int64_t)blockIdx.x * W + wave) * 8;
   const int rows_valid = (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
 
   // ---- 1. activation rows into LDS (LDS-DMA: lane l of an instruction
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t* __restrict__
   // last instruction of a row never writes into the next row's bytes.
   const int row_used = nwin * 256;
   const int chunks = (row_used + 1023) / 1024;
-  for (int m = wave; m < M; m += 4) {
+  for (int m = wave; m < M; m += W) {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2u);
     int8_t* dst = xs + w8a16_row_offset(m, row_bytes);
     for (int c = 0; c < chunks; ++c)
@@ -194,7 +197,8 @@ __global__ __launch_bounds__(256) void w8a16_kernel(const uint16_t* __restrict__
 
 template <bool HAS_BIAS, bool TWO>
 hipError_t launch_w8a16_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.N + 31) / 32)), block(256);
+  const RowGroupGrid g = row_group_grid(a.N);
+  const dim3 grid(g.blocks), block(64 * g.waves);
   const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)w8a16_row_bytes(a.K);
   const int vf = epilogue_vec_flags(a);
   if (a.K > 128 * kD)
