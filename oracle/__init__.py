@@ -11,6 +11,10 @@ from .w8a8_oracle import (  # noqa: F401
     K_MAX,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    f16_bits_to_f32,
+    f32_to_f16_bits,
+    to_f32,
+    from_f32,
     quant_rows,
     quant_act,
     quantize_weights,

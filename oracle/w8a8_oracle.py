@@ -46,6 +46,11 @@ the HIP path must reproduce):
   K <= 133 144.
 * subnormal inputs are legal and are not flushed; NaN/Inf inputs are outside
   the contract.
+* fp16 activations, weights, bias and output (the guide quantises "BF16/FP16"
+  weights; the Issue 5 probe, "Round one", runs bf16 and fp16 activations):
+  the same maths with fp16 in place of bf16. Inputs convert exactly to fp32;
+  y is the fp16 round to nearest even of the same fp32 value, and a value
+  past the largest finite fp16 rounds to infinity as IEEE rounding does.
 
 Parity pins: every function here is checked by tests that do not call it
 back (hand-computed golden files, exact rational arithmetic, brute force,
@@ -87,6 +92,34 @@ def f32_to_bf16_bits(t) -> np.ndarray:
     return r
 
 
+# --- fp16 <-> fp32 -------------------------------------------------------
+
+def f16_bits_to_f32(bits) -> np.ndarray:
+    """fp16 bit patterns -> fp32 values (exact: every fp16 value is an fp32 value)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def f32_to_f16_bits(t) -> np.ndarray:
+    """fp32 -> fp16 bit patterns by numpy's IEEE cast: round to nearest, ties to
+    even, subnormal results kept, overflow to infinity."""
+    with np.errstate(over="ignore"):          # overflow to infinity is the rule
+        return np.asarray(t, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+_TO_F32 = {"bf16": bf16_bits_to_f32, "f16": f16_bits_to_f32}
+_FROM_F32 = {"bf16": f32_to_bf16_bits, "f16": f32_to_f16_bits}
+
+
+def to_f32(bits, dtype: str = "bf16") -> np.ndarray:
+    """16-bit input bit patterns of type dtype ('bf16' or 'f16') -> fp32."""
+    return _TO_F32[dtype](bits)
+
+
+def from_f32(t, dtype: str = "bf16") -> np.ndarray:
+    """fp32 -> 16-bit output bit patterns of type dtype, round to nearest even."""
+    return _FROM_F32[dtype](t)
+
+
 # --- step 1/2: symmetric per-row int8 quantisation -----------------------
 
 def quant_rows(rows_f32) -> tuple[np.ndarray, np.ndarray]:
@@ -113,16 +146,17 @@ def quant_rows(rows_f32) -> tuple[np.ndarray, np.ndarray]:
     return q, scale
 
 
-def quant_act(x_bits) -> tuple[np.ndarray, np.ndarray]:
-    """Dynamic per-token quantisation of bf16 activations [M,K]."""
-    return quant_rows(bf16_bits_to_f32(x_bits))
+def quant_act(x_bits, dtype: str = "bf16") -> tuple[np.ndarray, np.ndarray]:
+    """Dynamic per-token quantisation of bf16 (or fp16) activations [M,K]."""
+    return quant_rows(to_f32(x_bits, dtype))
 
 
-def quantize_weights(w_bits) -> tuple[np.ndarray, np.ndarray]:
-    """Load-time per-output-channel quantisation of bf16 weights [N,K]
-    (Int8 Quantization guide, "Overview": quantise BF16/FP16 weights at load).
+def quantize_weights(w_bits, dtype: str = "bf16") -> tuple[np.ndarray, np.ndarray]:
+    """Load-time per-output-channel quantisation of bf16 (or fp16) weights
+    [N,K] (Int8 Quantization guide, "Overview": quantise BF16/FP16 weights at
+    load).
     """
-    return quant_rows(bf16_bits_to_f32(w_bits))
+    return quant_rows(to_f32(w_bits, dtype))
 
 
 # --- step 3: int8 x int8 -> int32 ----------------------------------------
@@ -162,37 +196,39 @@ def gemm_int64_rows(q, wq, rows=None) -> np.ndarray:
 
 # --- step 4: epilogue ----------------------------------------------------
 
-def epilogue_f32(acc, s_a, s_w, bias_bits=None) -> np.ndarray:
-    """fp32 value before the bf16 cast: ((fl32(acc) * s_a) * s_w) + bias.
+def epilogue_f32(acc, s_a, s_w, bias_bits=None, dtype: str = "bf16") -> np.ndarray:
+    """fp32 value before the output cast: ((fl32(acc) * s_a) * s_w) + bias.
 
     Issue 5 probe, "Round two": the result must carry act_scale (and the
-    per-channel weight scale). Each operation rounds to fp32 separately.
+    per-channel weight scale). Each operation rounds to fp32 separately. The
+    bias has the output type dtype.
     """
     t = np.asarray(acc, dtype=np.int32).astype(np.float32)   # RNE beyond 2^24
     t = t * np.asarray(s_a, dtype=np.float32)[:, None]
     t = t * np.asarray(s_w, dtype=np.float32)[None, :]
     if bias_bits is not None:
-        t = t + bf16_bits_to_f32(bias_bits)[None, :]
+        t = t + to_f32(bias_bits, dtype)[None, :]
     assert t.dtype == np.float32
     return t
 
 
-def epilogue(acc, s_a, s_w, bias_bits=None) -> np.ndarray:
-    """bf16 output bits of the epilogue."""
-    return f32_to_bf16_bits(epilogue_f32(acc, s_a, s_w, bias_bits))
+def epilogue(acc, s_a, s_w, bias_bits=None, dtype: str = "bf16") -> np.ndarray:
+    """Output bits (bf16 or fp16) of the epilogue."""
+    return from_f32(epilogue_f32(acc, s_a, s_w, bias_bits, dtype), dtype)
 
 
 # --- whole layer ---------------------------------------------------------
 
-def linear(x_bits, wq, s_w, bias_bits=None) -> dict:
-    """W8A8 linear of bf16 x [M,K] with prepared int8 weights [N,K], fp32 s_w.
+def linear(x_bits, wq, s_w, bias_bits=None, dtype: str = "bf16") -> dict:
+    """W8A8 linear of x [M,K] (bf16, or fp16 with dtype='f16') with prepared
+    int8 weights [N,K], fp32 s_w; bias and y have the type of x.
 
-    Returns xq, s_a, acc (int32) and y (bf16 bits) so every intermediate can
-    be compared.
+    Returns xq, s_a, acc (int32) and y (16-bit bits) so every intermediate
+    can be compared.
     """
-    xq, s_a = quant_act(x_bits)
+    xq, s_a = quant_act(x_bits, dtype)
     acc = gemm_exact(xq, wq)
-    y = epilogue(acc, s_a, s_w, bias_bits)
+    y = epilogue(acc, s_a, s_w, bias_bits, dtype)
     return {"xq": xq, "s_a": s_a, "acc": acc, "y": y}
 
 

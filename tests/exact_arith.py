@@ -74,3 +74,34 @@ def to_bf16_bits(r: Fraction) -> int:
     if n < 128:                                # subnormal (e == -126)
         return sign | n
     return sign | ((e + 127) << 7) | (n - 128)
+
+
+F16_MIN_EXP = -14           # smallest normal exponent of binary16
+F16_MANT = 10               # fraction bits of binary16
+
+
+def to_f16_bits(r: Fraction) -> int:
+    """Nearest IEEE binary16 to r (ties to even), as its 16-bit pattern.
+
+    Rounds as if the exponent range were unbounded above, then a result past
+    the largest finite value (65504) is infinity, which is the IEEE rule
+    (everything from 65520 up overflows). Subnormals are kept.
+    """
+    if r == 0:
+        return 0
+    sign = 0x8000 if r < 0 else 0
+    a = abs(r)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, F16_MIN_EXP)
+    quantum = Fraction(2) ** (e - F16_MANT)
+    n = round_half_even(a / quantum)          # significand in units of quantum
+    if n == 2 * 2**F16_MANT:                   # carried into the next binade
+        n = 2**F16_MANT
+        e += 1
+    if e > 15:
+        return sign | 0x7C00                   # infinity
+    if n < 2**F16_MANT:                        # subnormal (e == -14)
+        return sign | n
+    return sign | ((e + 15) << F16_MANT) | (n - 2**F16_MANT)

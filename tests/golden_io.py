@@ -66,3 +66,21 @@ def w8a16_cases():
         out.append(([_num(t) for t in xs.split()], [int(t) for t in ws.split()], _num(s),
                     None if b == "-" else int(b, 16), int(y, 16)))
     return out
+
+
+def f16_cases():
+    """({'quant': [(x values, scale, q values)], 'epi': [(acc, s_a, s_w,
+    bias_bits or None, y_bits)]}) from f16_hand_cases.txt."""
+    out = {"quant": [], "epi": []}
+    for line in _lines("f16_hand_cases.txt"):
+        tag, *rest = (p.strip() for p in line.split("|"))
+        if tag == "quant":
+            xs, s, qs = rest
+            out["quant"].append(([_num(t) for t in xs.split()], _num(s),
+                                 [int(t) for t in qs.split()]))
+        else:
+            lhs, y = rest
+            acc, sa, sw, b = lhs.split()
+            out["epi"].append((int(acc), _num(sa), _num(sw), None if b == "-" else int(b, 16),
+                               int(y, 16)))
+    return out
