@@ -130,6 +130,8 @@ def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
 def next_rows(w8, torch, np, dev, to_dev) -> dict:
     """The layers beyond the block step, measured after it on their own.
 
+    fp16 activations/outputs: the whole linear in fp16 against bf16 on the
+    DiT QKV shape and the modulation projection (M = 1, 16).
     Modulation projection 3072->18432 at M = 1, 8, 16 with bias: W8A16
     (bf16 activations, int8 weights) against the W8A8 small-M kernel, both
     HBM-bound (the weight is read once), reported as algorithmic GB/s =
@@ -185,6 +187,39 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
             "w8a8_us": us8, "w8a8_gbs": alg / (us8 * 1e-6) / 1e9,
             "w8a8_pct_hbm": 100 * alg / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS}
     del wqs
+
+    # fp16 activations/outputs: the whole linear (quantisation + product +
+    # epilogue), fp16 against bf16 on the same shapes and values.
+    def linear_pair(M, K, N, with_bias, seed):
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        x32 = torch.randn((M, K), generator=g)
+        w32 = torch.randn((N, K), generator=g) * 0.02
+        b32 = torch.randn((N,), generator=g) * 0.01 if with_bias else None
+        r = {}
+        for tag, dt, fn in (("bf16", torch.bfloat16, lib.w8a8_linear),
+                            ("f16", torch.float16, lib.w8a8_linear_f16)):
+            xx = x32.to(dt).to(dev)
+            wq_, sw_ = w8.quantize_weights(w32.to(dt).to(dev))
+            bb = None if b32 is None else b32.to(dt).to(dev)
+            oo = torch.empty((M, N), dtype=dt, device=dev)
+            wsz = torch.empty((w8.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            us = timed(lambda i: ok(fn(
+                xx.data_ptr(), M, K, K, wq_.data_ptr(), sw_.data_ptr(), N,
+                None if bb is None else bb.data_ptr(), oo.data_ptr(), N, wsz.data_ptr(),
+                wsz.numel(), None, sp.cuda_stream)), calls=20 if M > 16 else 60)
+            r[f"{tag}_us"] = us
+            if M > 16:
+                r[f"{tag}_tops"] = 2 * M * N * K / (us * 1e-6) / 1e12
+            del xx, wq_, sw_, bb, oo, wsz
+        return r
+
+    res["f16_linear"] = {
+        "note": "whole linear per call, same shapes and values in both types",
+        "qkv_4352x3072x9216": linear_pair(4352, 3072, 9216, False, 1),
+        "mod_m1_3072x18432": linear_pair(1, 3072, 18432, True, 2),
+        "mod_m16_3072x18432": linear_pair(16, 3072, 18432, True, 3),
+    }
     n_pk = 5
     packed0 = (wq0.to(torch.int16) + 128).to(torch.uint8).view(torch.int32)
     packs = [packed0] + [packed0.clone() for _ in range(n_pk - 1)]

@@ -131,6 +131,33 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 #define W8A8_ALIGN256(b) ((((size_t)(b)) + 255u) & ~(size_t)255u)
 
 /*
+ * fp16 variants ("Int8 Quantization" guide, "Overview": BF16/FP16 weights
+ * are quantised at load time; Issue 5 probe, "Round one": the layers run with
+ * bf16 and with fp16 activations). Each has the signature, layouts,
+ * requirements and errors of the bf16 entry point of the same name, with
+ * every 16-bit floating-point buffer (w, x, bias, out) holding IEEE binary16
+ * bit patterns instead of bf16. The arithmetic is the same: inputs convert
+ * exactly to fp32; scales are fp32; y = fp16_round_to_nearest_even(
+ * ((fl32(acc) * a_scale) * w_scale) + bias), subnormal results kept, and a
+ * value past the largest finite fp16 (65504; from 65520 up) becomes +-inf.
+ * wq / w_scale / xq / a_scale are the same int8 / fp32 buffers as for bf16,
+ * so weights prepared by either quantiser serve either type.
+ */
+int w8a8_quantize_weights_f16(const uint16_t* w, int64_t N, int64_t K, int64_t ldw,
+                              int8_t* wq, float* w_scale, void* stream);
+int w8a8_quant_act_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                       int8_t* xq, float* a_scale, void* stream);
+int w8a8_scaled_mm_f16(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                       const int8_t* wq, const float* w_scale, int64_t N,
+                       const uint16_t* bias, uint16_t* out, int64_t ldo,
+                       int32_t* acc_debug, void* stream);
+int w8a8_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                    const int8_t* wq, const float* w_scale, int64_t N,
+                    const uint16_t* bias, uint16_t* out, int64_t ldo,
+                    void* workspace, size_t workspace_bytes,
+                    int32_t* acc_debug, void* stream);
+
+/*
  * compressed-tensors pack-quantized ingest (Issue 5 probe, "Round one: int8
  * weight-only via compressed-tensors": weights stored with pack_to_int32, as
  * uint8 biased by 128, four per int32).

@@ -119,6 +119,25 @@ def make_linear_inputs(spec: LinearSpec | str, M: int | None = None) -> dict:
             "x": x, "w": w, "bias": bias}
 
 
+def to_f16_bits(a) -> np.ndarray:
+    """float64/float32 array -> IEEE fp16 bit patterns (uint16), RNE casts via
+    fp32 (numpy's cast; values past 65504 become infinity)."""
+    f32 = np.asarray(a, dtype=np.float64).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return f32.astype(np.float16).view(np.uint16).copy()
+
+
+def random_f16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
+    """Plain N(0, std^2) fp16 bits, for the fp16 parity cases."""
+    return to_f16_bits(rng.normal(0.0, std, size=shape))
+
+
+def all_finite_f16() -> np.ndarray:
+    """Every finite fp16 bit pattern (both zeros included): 63 488 values."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    return bits[((bits >> 10) & 0x1F) != 0x1F]
+
+
 def random_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     """Plain N(0, std^2) bf16 bits, for small parity cases of any shape."""
     return to_bf16_bits(rng.normal(0.0, std, size=shape))

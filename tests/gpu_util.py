@@ -62,3 +62,8 @@ def assert_equal(got, exp, what: str) -> None:
         first = tuple(bad[0]) if bad.size else None
         raise AssertionError(f"{what}: {len(bad)} mismatches, first at {first}: "
                              f"got {got[first] if first else None} exp {exp[first] if first else None}")
+
+
+def dev_f16(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16).cuda()

@@ -43,7 +43,8 @@ def q(fn, *args):
     return getattr(w8.lib(), fn)(*args)
 
 
-@pytest.mark.parametrize("fn", ["w8a8_quant_act", "w8a8_quantize_weights"])
+@pytest.mark.parametrize("fn", ["w8a8_quant_act", "w8a8_quantize_weights",
+                                "w8a8_quant_act_f16", "w8a8_quantize_weights_f16"])
 def test_quant_validation(fn):
     ok = (P(A), 4, 64, 64, P(A), P(A), None)
     assert q(fn, P(A), -1, 64, 64, P(A), P(A), None) == w8.ERR_INVALID_ARG
@@ -63,8 +64,8 @@ def test_quant_validation(fn):
     assert ok  # the valid call itself would launch; it is exercised on the GPU
 
 
-def test_scaled_mm_validation():
-    f = "w8a8_scaled_mm"
+@pytest.mark.parametrize("f", ["w8a8_scaled_mm", "w8a8_scaled_mm_f16"])
+def test_scaled_mm_validation(f):
     base = [P(A), P(A), 4, 64, P(A), P(A), 8, None, P(A), 8, None, None]
 
     def call(**kw):
@@ -92,8 +93,8 @@ def test_scaled_mm_validation():
     assert call(M=0, xq=None, sa=None, wq=None, sw=None, out=None) == w8.OK
 
 
-def test_linear_validation():
-    f = "w8a8_linear"
+@pytest.mark.parametrize("f", ["w8a8_linear", "w8a8_linear_f16"])
+def test_linear_validation(f):
     M, K, N = 32, 64, 8
     ws = w8.workspace_bytes(M, K, N)
     base = [P(A), M, K, K, P(A), P(A), N, None, P(A), N, P(A), ws, None, None]
@@ -204,3 +205,7 @@ def test_binding_refuses_cpu_tensors():
         w8.quant_act(torch.zeros((2, 16), dtype=torch.bfloat16))
     with pytest.raises(TypeError):
         w8.quant_act(torch.zeros((2, 16), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        w8.quant_act(torch.zeros((2, 16), dtype=torch.float16))
+    with pytest.raises(TypeError):
+        w8.quantize_weights(torch.zeros((2, 16), dtype=torch.float64))

@@ -6,8 +6,9 @@ every step of the layer runs in the library's HIP kernels. PyTorch supplies
 device memory and streams. If the library is missing the functions raise:
 there is no fallback.
 
-    wq, w_scale = quantize_weights(w)              # load time, bf16 [N, K]
+    wq, w_scale = quantize_weights(w)              # load time, bf16/fp16 [N, K]
     y = linear(x, wq, w_scale, bias)               # bf16 [M, K] -> bf16 [M, N]
+                                                   # (fp16 in -> fp16 out)
     xq, a_scale = quant_act(x)                     # the two ops separately
     y = scaled_mm(xq, a_scale, wq, w_scale, bias)
     wq, w_scale = unpack_pack_quantized(packed, scale)  # compressed-tensors ingest
@@ -40,6 +41,10 @@ SYMBOLS = (
     "w8a8_quant_act",
     "w8a8_scaled_mm",
     "w8a8_linear",
+    "w8a8_quantize_weights_f16",
+    "w8a8_quant_act_f16",
+    "w8a8_scaled_mm_f16",
+    "w8a8_linear_f16",
     "w8a8_linear_workspace_bytes",
     "w8a8_linear_path",
     "w8a8_gemm_tile",
@@ -77,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.w8a8_quant_act.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     L.w8a8_scaled_mm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, i64, vp, vp]
     L.w8a8_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp, sz, vp, vp]
+    L.w8a8_quantize_weights_f16.argtypes = L.w8a8_quantize_weights.argtypes
+    L.w8a8_quant_act_f16.argtypes = L.w8a8_quant_act.argtypes
+    L.w8a8_scaled_mm_f16.argtypes = L.w8a8_scaled_mm.argtypes
+    L.w8a8_linear_f16.argtypes = L.w8a8_linear.argtypes
     L.w8a8_linear_workspace_bytes.argtypes = [i64, i64, i64]
     L.w8a8_linear_workspace_bytes.restype = sz
     L.w8a8_linear_path.argtypes = [i64, i64, i64]
@@ -87,6 +96,8 @@ def lib() -> ctypes.CDLL:
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for name in ("w8a8_quantize_weights", "w8a8_quant_act", "w8a8_scaled_mm", "w8a8_linear",
+                 "w8a8_quantize_weights_f16", "w8a8_quant_act_f16", "w8a8_scaled_mm_f16",
+                 "w8a8_linear_f16",
                  "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized", "w8a16_linear",
                  "w8a8_last_hip_error"):
         getattr(L, name).restype = ci
@@ -128,6 +139,16 @@ def _rows(t: torch.Tensor, dtype, name: str):
     return t.shape[0], t.shape[1], ld
 
 
+# 16-bit floating-point types of x / w / bias / out and the entry-point suffix
+_HALF = {torch.bfloat16: "", torch.float16: "_f16"}
+
+
+def _half(dtype, name: str) -> str:
+    if dtype not in _HALF:
+        raise TypeError(f"{name} must be bfloat16 or float16, got {dtype}")
+    return _HALF[dtype]
+
+
 def _vec(t, dtype, n, name):
     if t is None:
         return None
@@ -139,50 +160,54 @@ def _vec(t, dtype, n, name):
 
 
 def quantize_weights(w: torch.Tensor):
-    """bf16 W [N, K] -> (wq int8 [N, K], w_scale fp32 [N])."""
-    N, K, ld = _rows(w, torch.bfloat16, "w")
+    """bf16 or fp16 W [N, K] -> (wq int8 [N, K], w_scale fp32 [N])."""
+    fn = "w8a8_quantize_weights" + _half(w.dtype, "w")
+    N, K, ld = _rows(w, w.dtype, "w")
     wq = torch.empty((N, K), dtype=torch.int8, device=w.device)
     s = torch.empty((N,), dtype=torch.float32, device=w.device)
-    _check("w8a8_quantize_weights",
-           lib().w8a8_quantize_weights(_ptr(w), N, K, ld, _ptr(wq), _ptr(s), _stream(w.device)))
+    _check(fn, getattr(lib(), fn)(_ptr(w), N, K, ld, _ptr(wq), _ptr(s), _stream(w.device)))
     return wq, s
 
 
 def quant_act(x: torch.Tensor):
-    """bf16 x [M, K] -> (xq int8 [M, K], a_scale fp32 [M])."""
-    M, K, ld = _rows(x, torch.bfloat16, "x")
+    """bf16 or fp16 x [M, K] -> (xq int8 [M, K], a_scale fp32 [M])."""
+    fn = "w8a8_quant_act" + _half(x.dtype, "x")
+    M, K, ld = _rows(x, x.dtype, "x")
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     s = torch.empty((M,), dtype=torch.float32, device=x.device)
-    _check("w8a8_quant_act",
-           lib().w8a8_quant_act(_ptr(x), M, K, ld, _ptr(xq), _ptr(s), _stream(x.device)))
+    _check(fn, getattr(lib(), fn)(_ptr(x), M, K, ld, _ptr(xq), _ptr(s), _stream(x.device)))
     return xq, s
 
 
-def scaled_mm(xq, a_scale, wq, w_scale, bias=None, out=None, acc_debug=None):
-    """int8 xq [M,K] x int8 wq [N,K] -> bf16 [M,N] with the scale epilogue.
+def scaled_mm(xq, a_scale, wq, w_scale, bias=None, out=None, acc_debug=None,
+              dtype=torch.bfloat16):
+    """int8 xq [M,K] x int8 wq [N,K] -> [M,N] of `dtype` (bf16 or fp16; the
+    type of `out` when given) with the scale epilogue; bias has that type.
 
     acc_debug: optional int32 [M, N] tensor that receives the raw
     accumulators from the same kernel.
     """
+    if out is not None:
+        dtype = out.dtype
+    fn = "w8a8_scaled_mm" + _half(dtype, "out")
     M, K, ldq = _rows(xq, torch.int8, "xq")
     N, K2, ldw = _rows(wq, torch.int8, "wq")
     if K2 != K or (M > 1 and ldq != K) or (N > 1 and ldw != K):
         raise ValueError("xq and wq must be contiguous [*, K] with the same K")
     _vec(a_scale, torch.float32, M, "a_scale")
     _vec(w_scale, torch.float32, N, "w_scale")
-    _vec(bias, torch.bfloat16, N, "bias")
+    _vec(bias, dtype, N, "bias")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    Mo, No, ldo = _rows(out, torch.bfloat16, "out")
+        out = torch.empty((M, N), dtype=dtype, device=xq.device)
+    Mo, No, ldo = _rows(out, dtype, "out")
     if (Mo, No) != (M, N):
         raise ValueError("out must be [M, N]")
     if acc_debug is not None and (acc_debug.shape != (M, N) or acc_debug.dtype != torch.int32
                                   or not acc_debug.is_contiguous()):
         raise ValueError("acc_debug must be a contiguous int32 [M, N] tensor")
-    _check("w8a8_scaled_mm",
-           lib().w8a8_scaled_mm(_ptr(xq), _ptr(a_scale), M, K, _ptr(wq), _ptr(w_scale), N,
-                                _ptr(bias), _ptr(out), ldo, _ptr(acc_debug),
-                                _stream(xq.device)))
+    _check(fn, getattr(lib(), fn)(_ptr(xq), _ptr(a_scale), M, K, _ptr(wq), _ptr(w_scale), N,
+                                  _ptr(bias), _ptr(out), ldo, _ptr(acc_debug),
+                                  _stream(xq.device)))
     return out
 
 
@@ -254,20 +279,22 @@ def workspace_views(workspace: torch.Tensor, M: int, K: int):
 
 
 def linear(x, wq, w_scale, bias=None, out=None, workspace=None, acc_debug=None):
-    """W8A8 linear: bf16 x [M, K] -> bf16 [M, N].
+    """W8A8 linear: bf16 x [M, K] -> bf16 [M, N] (fp16 x -> fp16 y; bias and
+    out have the type of x).
 
     workspace: optional uint8 GPU tensor of at least workspace_bytes(M,K,N)
     bytes; after the call it holds xq and a_scale (see workspace_views).
     """
-    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    fn = "w8a8_linear" + _half(x.dtype, "x")
+    M, K, ldx = _rows(x, x.dtype, "x")
     N, K2, ldw = _rows(wq, torch.int8, "wq")
     if K2 != K or (N > 1 and ldw != K):
         raise ValueError("wq must be contiguous [N, K] with the K of x")
     _vec(w_scale, torch.float32, N, "w_scale")
-    _vec(bias, torch.bfloat16, N, "bias")
+    _vec(bias, x.dtype, N, "bias")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    Mo, No, ldo = _rows(out, torch.bfloat16, "out")
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    Mo, No, ldo = _rows(out, x.dtype, "out")
     if (Mo, No) != (M, N):
         raise ValueError("out must be [M, N]")
     need = workspace_bytes(M, K, N)
@@ -278,8 +305,7 @@ def linear(x, wq, w_scale, bias=None, out=None, workspace=None, acc_debug=None):
     if acc_debug is not None and (acc_debug.shape != (M, N) or acc_debug.dtype != torch.int32
                                   or not acc_debug.is_contiguous()):
         raise ValueError("acc_debug must be a contiguous int32 [M, N] tensor")
-    _check("w8a8_linear",
-           lib().w8a8_linear(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
-                             _ptr(out), ldo, _ptr(workspace), workspace.numel(),
-                             _ptr(acc_debug), _stream(x.device)))
+    _check(fn, getattr(lib(), fn)(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
+                                  _ptr(out), ldo, _ptr(workspace), workspace.numel(),
+                                  _ptr(acc_debug), _stream(x.device)))
     return out

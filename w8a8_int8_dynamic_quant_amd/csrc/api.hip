@@ -31,14 +31,14 @@ int hip_status(hipError_t e) {
 }
 
 int quant_common(const uint16_t* x, int64_t R, int64_t K, int64_t ld, int8_t* q, float* scale,
-                 void* stream) {
+                 void* stream, bool f16) {
   if (R < 0) return W8A8_ERR_INVALID_ARG;
   if (int s = check_k(K)) return s;
   if (int s = check_bf16_ld(ld, K)) return s;
   if (R == 0) return W8A8_OK;
   if (!x || !q || !scale) return W8A8_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return W8A8_ERR_MISALIGNED;
-  return hip_status(w8a8::launch_quant_rows(x, R, K, ld, q, scale, (hipStream_t)stream));
+  return hip_status(w8a8::launch_quant_rows(x, R, K, ld, q, scale, (hipStream_t)stream, f16));
 }
 
 // Checks shared by the two GEMM entry points (everything but x / xq).
@@ -59,29 +59,75 @@ bool small_m_path(int64_t M, int64_t K) {
   return M >= 1 && M <= W8A8_SMALL_M && K <= w8a8::kSmallMMaxK;
 }
 
+int scaled_mm_common(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                     const int8_t* wq, const float* w_scale, int64_t N, const uint16_t* bias,
+                     uint16_t* out, int64_t ldo, int32_t* acc_debug, void* stream, bool f16) {
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!xq || !a_scale) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(a_scale, 4)) return W8A8_ERR_MISALIGNED;
+  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo, f16};
+  return hip_status(w8a8::launch_gemm(g, (hipStream_t)stream));
+}
+
+int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                  const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
+                  int64_t ldo, void* workspace, size_t workspace_bytes, int32_t* acc_debug,
+                  void* stream, bool f16) {
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
+  if (int s = check_bf16_ld(ldx, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!x) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < w8a8_linear_workspace_bytes(M, K, N))
+    return W8A8_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return W8A8_ERR_MISALIGNED;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* a_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            W8A8_ALIGN256((size_t)M * (size_t)K));
+  hipStream_t st = (hipStream_t)stream;
+  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo, f16};
+  if (small_m_path(M, K)) return hip_status(w8a8::launch_small_m(x, ldx, g, xq, a_scale, st));
+  if (int s = hip_status(w8a8::launch_quant_rows(x, M, K, ldx, xq, a_scale, st, f16))) return s;
+  return hip_status(w8a8::launch_gemm(g, st));
+}
+
 }  // namespace
 
 extern "C" {
 
 int w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wq,
                           float* w_scale, void* stream) {
-  return quant_common(w, N, K, ldw, wq, w_scale, stream);
+  return quant_common(w, N, K, ldw, wq, w_scale, stream, false);
 }
 
 int w8a8_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* xq,
                    float* a_scale, void* stream) {
-  return quant_common(x, M, K, ldx, xq, a_scale, stream);
+  return quant_common(x, M, K, ldx, xq, a_scale, stream, false);
 }
 
 int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
                    const int8_t* wq, const float* w_scale, int64_t N, const uint16_t* bias,
                    uint16_t* out, int64_t ldo, int32_t* acc_debug, void* stream) {
-  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
-  if (M == 0) return W8A8_OK;
-  if (!xq || !a_scale) return W8A8_ERR_INVALID_ARG;
-  if (!aligned(xq, 16) || !aligned(a_scale, 4)) return W8A8_ERR_MISALIGNED;
-  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo};
-  return hip_status(w8a8::launch_gemm(g, (hipStream_t)stream));
+  return scaled_mm_common(xq, a_scale, M, K, wq, w_scale, N, bias, out, ldo, acc_debug, stream,
+                          false);
+}
+
+int w8a8_quantize_weights_f16(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wq,
+                              float* w_scale, void* stream) {
+  return quant_common(w, N, K, ldw, wq, w_scale, stream, true);
+}
+
+int w8a8_quant_act_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* xq,
+                       float* a_scale, void* stream) {
+  return quant_common(x, M, K, ldx, xq, a_scale, stream, true);
+}
+
+int w8a8_scaled_mm_f16(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
+                       const int8_t* wq, const float* w_scale, int64_t N, const uint16_t* bias,
+                       uint16_t* out, int64_t ldo, int32_t* acc_debug, void* stream) {
+  return scaled_mm_common(xq, a_scale, M, K, wq, w_scale, N, bias, out, ldo, acc_debug, stream,
+                          true);
 }
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -108,22 +154,16 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8
                 const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
                 int64_t ldo, void* workspace, size_t workspace_bytes, int32_t* acc_debug,
                 void* stream) {
-  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
-  if (int s = check_bf16_ld(ldx, K)) return s;
-  if (M == 0) return W8A8_OK;
-  if (!x) return W8A8_ERR_INVALID_ARG;
-  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
-  if (!workspace || workspace_bytes < w8a8_linear_workspace_bytes(M, K, N))
-    return W8A8_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return W8A8_ERR_MISALIGNED;
-  int8_t* xq = static_cast<int8_t*>(workspace);
-  float* a_scale = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                            W8A8_ALIGN256((size_t)M * (size_t)K));
-  hipStream_t st = (hipStream_t)stream;
-  w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo};
-  if (small_m_path(M, K)) return hip_status(w8a8::launch_small_m(x, ldx, g, xq, a_scale, st));
-  if (int s = hip_status(w8a8::launch_quant_rows(x, M, K, ldx, xq, a_scale, st))) return s;
-  return hip_status(w8a8::launch_gemm(g, st));
+  return linear_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, workspace, workspace_bytes,
+                       acc_debug, stream, false);
+}
+
+int w8a8_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                    const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
+                    int64_t ldo, void* workspace, size_t workspace_bytes, int32_t* acc_debug,
+                    void* stream) {
+  return linear_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, workspace, workspace_bytes,
+                       acc_debug, stream, true);
 }
 
 int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int64_t ldp,

@@ -3,6 +3,7 @@
 // acc[m,n] = sum_k xq[m,k] * wq[n,k]   (int32, exact; unsloth commit log of
 //   test_diffusion_transformer_quant.py: int8 products, int32 accumulation)
 // y[m,n]   = bf16(((fl32(acc) * a_scale[m]) * w_scale[n]) + bias[n])
+//   (bias and y fp16 instead for fp16 layers; the same fp32 steps)
 //   (Issue 5 probe, "Round two": the int8 scaled-MM result carries act_scale
 //    and the fp32 per-channel weight scale)
 //
@@ -127,14 +128,22 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
-// Two fp32 -> two bf16 (round to nearest even) packed low/high, one
-// v_cvt_pk_bf16_f32 on gfx950.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const v2bf h = __builtin_convertvector((v2f){lo, hi}, v2bf);
-  return __builtin_bit_cast(uint32_t, h);
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (or fp16) values, round to nearest even, packed
+// low/high (v_cvt_pk_bf16_f32 on gfx950 for bf16).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+  if constexpr (F16) {
+    const v2h h = __builtin_convertvector((v2f){lo, hi}, v2h);
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    const v2bf h = __builtin_convertvector((v2f){lo, hi}, v2bf);
+    return __builtin_bit_cast(uint32_t, h);
+  }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS, bool F16>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArgs a, int tiles_m,
                                                                          int tiles_n, int vec_flags) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
     if constexpr (HAS_BIAS) {
       const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
       for (int t = tid; t < BN; t += 64 * NW)
-        lds_b[t] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_b, t * 2, 0, 0));
+        lds_b[t] = half_to_f32<F16>(__builtin_amdgcn_raw_buffer_load_b16(r_b, t * 2, 0, 0));
     }
   }
 
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
           const float t1 = epilogue_f32<HAS_BIAS>(c[4 * q + 1], sa[j], sw4.y, b4[1]);
           const float t2 = epilogue_f32<HAS_BIAS>(c[4 * q + 2], sa[j], sw4.z, b4[2]);
           const float t3 = epilogue_f32<HAS_BIAS>(c[4 * q + 3], sa[j], sw4.w, b4[3]);
-          visit(nl, ml, pack_bf16x2(t0, t1), pack_bf16x2(t2, t3));
+          visit(nl, ml, pack_half2<F16>(t0, t1), pack_half2<F16>(t2, t3));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -408,12 +417,17 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_m * tiles_n;
   const int vec_flags = epilogue_vec_flags(a);
   dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
-  if (a.bias)
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, true>), grid, block, 0,
-                       stream, a, (int)tiles_m, (int)tiles_n, vec_flags);
-  else
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, false>), grid, block, 0,
-                       stream, a, (int)tiles_m, (int)tiles_n, vec_flags);
+#define W8A8_GEMM(B, H)                                                                    \
+  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, B, H>), grid, block, 0, \
+                     stream, a, (int)tiles_m, (int)tiles_n, vec_flags)
+  if (a.f16) {
+    if (a.bias) W8A8_GEMM(true, true);
+    else W8A8_GEMM(false, true);
+  } else {
+    if (a.bias) W8A8_GEMM(true, false);
+    else W8A8_GEMM(false, false);
+  }
+#undef W8A8_GEMM
   return hipGetLastError();
 }
 

@@ -1,4 +1,4 @@
-// Per-row symmetric int8 quantisation of bf16 rows (gfx950).
+// Per-row symmetric int8 quantisation of bf16 or fp16 rows (gfx950).
 //
 // Serves both the dynamic per-token activation quantisation and the
 // load-time per-output-channel weight quantisation of the W8A8 int8-dynamic
@@ -11,7 +11,7 @@
 // of 4 waves quantises one row at a time and walks over rows
 // blockIdx.x, blockIdx.x + gridDim.x, ...; the grid is sized so that every
 // workgroup is resident and all do the same number of rows. Thread t holds
-// the row's 16-byte chunks t, t+256, ... (8 bf16 each; 4 KiB contiguous per
+// the row's 16-byte chunks t, t+256, ... (8 values each; 4 KiB contiguous per
 // load instruction of the workgroup) in registers, read through a buffer
 // descriptor bounded at the row end, so chunks past K read as zero (which
 // leaves amax unchanged) without any branch. amax is an integer max over
@@ -73,7 +73,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int CHT>
+template <int CHT, bool F16>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
     lds_barrier();
     if (row + stride < R) load_row(row + stride, nxt);
     amax = max(max(wmax[parity][0], wmax[parity][1]), max(wmax[parity][2], wmax[parity][3]));
-    const float s = row_scale(amax);
+    const float s = row_scale<F16>(amax);
     const bool zero = (amax == 0);
     const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;  // subnormal s
     const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 #pragma unroll
     for (int u = 0; u < CHT; ++u) {
       const uint32_t idx = (uint32_t)(tid + 256 * u);
-      store8(quant8(cur[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
+      store8(quant8<F16>(cur[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
     }
     if (tid == 0) scale[row] = s;
   };
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
 // requested at once and kept in registers between the amax and the quantise
 // step; all rows are in flight together. With P = 2 the two waves exchange
 // their amax through LDS.
-template <int CHUNKS, int P>
+template <int CHUNKS, int P, bool F16>
 __global__ __launch_bounds__(256) void quant_rows_wave_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -162,14 +162,14 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(
     if (!valid) return;
   }
   const __amdgpu_buffer_rsrc_t rq = row_rsrc(q + row * K, (uint32_t)K);
-  const float s = row_scale(amax);
+  const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;  // subnormal s
   const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) {
     const uint32_t idx = (uint32_t)(lane + 64 * (c + CHUNKS * part));
-    store8(quant8(v[c], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
+    store8(quant8<F16>(v[c], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
   }
   if (lane == 0 && part == 0) scale[row] = s;
 }
@@ -177,6 +177,7 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(
 // Rows longer than the register-resident limit: one wave per row, an amax
 // pass, then a second pass that re-reads the row (from L2 for the row
 // lengths that get here).
+template <bool F16>
 __global__ __launch_bounds__(256) void quant_rows_long_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
     for (int u = 0; u < U; ++u) amax = absmax_bits8(v[u], amax);
   }
   amax = wave_max_dpp(amax);
-  const float s = row_scale(amax);
+  const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
   const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t idx = base + lane + 64 * u;
-      store8(quant8(v[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
+      store8(quant8<F16>(v[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
     }
   }
   if (lane == 0) scale[row] = s;
@@ -224,30 +225,30 @@ int resident_workgroups(const void* kernel) {
   return cus * per_cu;
 }
 
-template <int C>
+template <int C, bool F16>
 hipError_t launch_cht(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, int8_t* q, float* scale,
                       hipStream_t stream) {
   static int resident = 0;               // per kernel; the same value on every device here
-  if (resident == 0) resident = resident_workgroups((const void*)quant_rows_kernel<C>);
+  if (resident == 0) resident = resident_workgroups((const void*)quant_rows_kernel<C, F16>);
   // as many resident workgroups as possible, each doing the same row count
   const int64_t rows_per_wg = (R + resident - 1) / resident;
   const dim3 grid((unsigned)((R + rows_per_wg - 1) / rows_per_wg)), block(256);
-  hipLaunchKernelGGL(quant_rows_kernel<C>, grid, block, 0, stream, x, R, K, ldx, q, scale);
+  hipLaunchKernelGGL((quant_rows_kernel<C, F16>), grid, block, 0, stream, x, R, K, ldx, q, scale);
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ldx,
-                             int8_t* q, float* scale, hipStream_t stream) {
+template <bool F16>
+hipError_t launch_quant_rows_t(const uint16_t* x, int64_t R, int64_t K, int64_t ldx,
+                               int8_t* q, float* scale, hipStream_t stream) {
   if (R == 0) return hipSuccess;
   const int64_t nchunks = K >> 3;
   const int64_t per_lane = (nchunks + 63) / 64;
   if (per_lane <= 8) {                    // K <= 4096: one or two waves per row
     const dim3 block(256);
-#define W8A8_QW(C, P)                                                                        \
-    hipLaunchKernelGGL((quant_rows_wave_kernel<C, P>), dim3((unsigned)((R + 4 / P - 1) / (4 / P))), \
-                       block, 0, stream, x, R, K, ldx, q, scale);                            \
+#define W8A8_QW(C, P)                                                                   \
+    hipLaunchKernelGGL((quant_rows_wave_kernel<C, P, F16>),                             \
+                       dim3((unsigned)((R + 4 / P - 1) / (4 / P))), block, 0, stream, x, R, \
+                       K, ldx, q, scale);                                               \
     return hipGetLastError();
     if (per_lane <= 1) { W8A8_QW(1, 1) }
     if (per_lane <= 2) { W8A8_QW(2, 1) }
@@ -257,14 +258,22 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ld
 #undef W8A8_QW
   }
   const int64_t per_thread = (nchunks + 255) / 256;
-  if (per_thread <= 4) return launch_cht<4>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 6) return launch_cht<6>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 8) return launch_cht<8>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 12) return launch_cht<12>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 16) return launch_cht<16>(x, R, K, ldx, q, scale, stream);
-  hipLaunchKernelGGL(quant_rows_long_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, x, R,
-                     K, ldx, q, scale);
+  if (per_thread <= 4) return launch_cht<4, F16>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 6) return launch_cht<6, F16>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 8) return launch_cht<8, F16>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 12) return launch_cht<12, F16>(x, R, K, ldx, q, scale, stream);
+  if (per_thread <= 16) return launch_cht<16, F16>(x, R, K, ldx, q, scale, stream);
+  hipLaunchKernelGGL(quant_rows_long_kernel<F16>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
+                     stream, x, R, K, ldx, q, scale);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, int8_t* q,
+                             float* scale, hipStream_t stream, bool f16) {
+  return f16 ? launch_quant_rows_t<true>(x, R, K, ldx, q, scale, stream)
+             : launch_quant_rows_t<false>(x, R, K, ldx, q, scale, stream);
 }
 
 }  // namespace w8a8

@@ -1,4 +1,5 @@
 // Small-M W8A8 linear (M <= 16): one fused, weight-streaming kernel (gfx950).
+// Activations, bias and output are bf16, or all fp16 (same arithmetic).
 //
 // The int8 matmul route of the prior art requires more than 16 activation
 // rows, so the AdaLN modulation and conditioning projections, which run at
@@ -78,20 +79,21 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Quantises the row chunks held in v (chunk lane + 64*u of the row, u < kQ)
 // with the row's scale; returns the scale.
+template <bool F16>
 __device__ __forceinline__ float quantise_regs(const uint4 (&v)[kQ], uint32_t nchunks, int lane,
                                                int8_t* xrow, int8_t* qrow, bool write_q) {
   uint32_t amax = 0;
 #pragma unroll
   for (int u = 0; u < kQ; ++u) amax = absmax_bits8(v[u], amax);
   amax = wave_max_u32(amax);
-  const float s = row_scale(amax);
+  const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
   const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
 #pragma unroll
   for (int u = 0; u < kQ; ++u) {
     const uint32_t idx = lane + 64 * u;
-    const uint2 q = quant8(v[u], s, r, zero, exact_div);
+    const uint2 q = quant8<F16>(v[u], s, r, zero, exact_div);
     if (idx < nchunks) {
       *reinterpret_cast<uint2*>(xrow + 8 * idx) = q;
       if (write_q) *reinterpret_cast<uint2*>(qrow + 8 * idx) = q;
@@ -102,6 +104,7 @@ __device__ __forceinline__ float quantise_regs(const uint4 (&v)[kQ], uint32_t nc
 
 // Rows longer than 64*kQ chunks: an amax pass, then a quantise pass that
 // reads the row again.
+template <bool F16>
 __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32_t nchunks, int lane,
                                                int8_t* xrow, int8_t* qrow, bool write_q) {
   constexpr int U = 8;
@@ -114,7 +117,7 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
     for (int u = 0; u < U; ++u) amax = absmax_bits8(w[u], amax);
   }
   amax = wave_max_u32(amax);
-  const float s = row_scale(amax);
+  const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
   const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
@@ -125,7 +128,7 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t idx = base + lane + 64 * u;
-      const uint2 q = quant8(w[u], s, r, zero, exact_div);
+      const uint2 q = quant8<F16>(w[u], s, r, zero, exact_div);
       if (idx < nchunks) {
         *reinterpret_cast<uint2*>(xrow + 8 * idx) = q;
         if (write_q) *reinterpret_cast<uint2*>(qrow + 8 * idx) = q;
@@ -136,7 +139,7 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
 }
 
 // Up to kMaxWaves waves per workgroup: three waves per SIMD.
-template <bool HAS_BIAS, bool TWO, int MODE>
+template <bool HAS_BIAS, bool TWO, int MODE, bool F16>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
     float* __restrict__ sa_out, int vec_flags) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();                       // ... and every other wave's
     issue_all();
     if (wave < M) {
-      const float s = quantise_regs(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
+      const float s = quantise_regs<F16>(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
                                     write_q);
       if (lane == 0) {
         sa_lds[wave] = s;
@@ -201,9 +204,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
         uint4 v[kQ];
 #pragma unroll
         for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
-        s = quantise_regs(v, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
+        s = quantise_regs<F16>(v, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
       } else {
-        s = quantise_long(rx, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
+        s = quantise_long<F16>(rx, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
       }
       if (lane == 0) {
         sa_lds[m] = s;
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   for (int r = 0; r < 4; ++r) {
     const bool ok = nl + r < rows_valid;
     sw[r] = ok ? a.w_scale[n + r] : 0.f;
-    bb[r] = (HAS_BIAS && ok) ? bf16_to_f32(a.bias[n + r]) : 0.f;
+    bb[r] = (HAS_BIAS && ok) ? half_to_f32<F16>(a.bias[n + r]) : 0.f;
   }
 #pragma unroll
   for (int blk = 0; blk < (TWO ? 2 : 1); ++blk) {
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     const float sa = sa_lds[m];
     uint32_t y[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[r] = f32_to_bf16_rne(epilogue_f32<HAS_BIAS>(c[r], sa, sw[r], bb[r]));
+    for (int r = 0; r < 4; ++r) y[r] = f32_to_half_rne<F16>(epilogue_f32<HAS_BIAS>(c[r], sa, sw[r], bb[r]));
     uint16_t* o = a.out + (int64_t)m * a.ldo + n;
     if (nl + 3 < rows_valid && (vec_flags & 1)) {
       *reinterpret_cast<uint2*>(o) = make_uint2(y[0] | (y[1] << 16), y[2] | (y[3] << 16));
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <bool HAS_BIAS, bool TWO>
+template <bool HAS_BIAS, bool TWO, bool F16>
 hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   const RowGroupGrid g = row_group_grid(a.N);
@@ -308,15 +311,25 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)xs_stride(a.K);
   const int vf = epilogue_vec_flags(a);
   if (a.K > kShortK)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, LONG>), grid, block, lds, stream, x, ldx, a,
-                       xq_out, a_scale_out, vf);
-  else if (a.M <= g.waves)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, ONE_ROW>), grid, block, lds, stream, x, ldx,
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, LONG, F16>), grid, block, lds, stream, x, ldx,
                        a, xq_out, a_scale_out, vf);
+  else if (a.M <= g.waves)
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, ONE_ROW, F16>), grid, block, lds, stream, x,
+                       ldx, a, xq_out, a_scale_out, vf);
   else
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT>), grid, block, lds, stream, x, ldx, a,
-                       xq_out, a_scale_out, vf);
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT, F16>), grid, block, lds, stream, x, ldx,
+                       a, xq_out, a_scale_out, vf);
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
+                        float* a_scale_out, hipStream_t stream) {
+  if (a.bias)
+    return a.M > 8 ? launch_variant<true, true, F16>(x, ldx, a, xq_out, a_scale_out, stream)
+                   : launch_variant<true, false, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  return a.M > 8 ? launch_variant<false, true, F16>(x, ldx, a, xq_out, a_scale_out, stream)
+                 : launch_variant<false, false, F16>(x, ldx, a, xq_out, a_scale_out, stream);
 }
 
 }  // namespace
@@ -324,11 +337,8 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
 hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  if (a.bias)
-    return a.M > 8 ? launch_variant<true, true>(x, ldx, a, xq_out, a_scale_out, stream)
-                   : launch_variant<true, false>(x, ldx, a, xq_out, a_scale_out, stream);
-  return a.M > 8 ? launch_variant<false, true>(x, ldx, a, xq_out, a_scale_out, stream)
-                 : launch_variant<false, false>(x, ldx, a, xq_out, a_scale_out, stream);
+  return a.f16 ? launch_dtype<true>(x, ldx, a, xq_out, a_scale_out, stream)
+               : launch_dtype<false>(x, ldx, a, xq_out, a_scale_out, stream);
 }
 
 }  // namespace w8a8

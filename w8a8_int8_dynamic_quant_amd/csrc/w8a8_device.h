@@ -4,6 +4,9 @@
 // epilogue of the W8A8 int8-dynamic linear; Issue 5 probe, "Round two"):
 //   scale = fl32(amax / 127); q = clamp(rint(fl32(x / scale)), -127, 127)
 //   y = bf16_rne(((fl32(acc) * s_a) * s_w) + bias)
+// The same maths serves fp16 activations/weights/bias/output (the guide's
+// "BF16/FP16" weights): every helper that reads or writes 16-bit values takes
+// the type as a template flag (F16 = false: bf16).
 // Everything here is compiled with -ffp-contract=off so that no product and
 // sum are fused, and with IEEE (correctly rounded) fp32 division.
 #pragma once
@@ -25,6 +28,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// fp16 bits -> fp32 (exact; fp16 subnormals are kept: the f16 denormal mode
+// of these kernels is IEEE).
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+template <bool F16>
+__device__ __forceinline__ float half_to_f32(uint32_t bits16) {
+  if constexpr (F16) return f16_to_f32(bits16);
+  else return bf16_to_f32(bits16);
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -33,10 +48,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// Per-row scale from the largest |x| bit pattern (bf16 magnitudes compare
-// as integers). One IEEE division.
+// fp32 -> fp16 bits by the hardware conversion (round to nearest even in the
+// default mode, subnormal results kept, overflow to infinity).
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint32_t f32_to_half_rne(float f) {
+  if constexpr (F16) return f32_to_f16_rne(f);
+  else return f32_to_bf16_rne(f);
+}
+
+// Per-row scale from the largest |x| bit pattern (bf16 and fp16 magnitudes
+// both compare as integers). One IEEE division.
+template <bool F16 = false>
 __device__ __forceinline__ float row_scale(uint32_t amax_bits16) {
-  return bf16_to_f32(amax_bits16) / 127.0f;
+  return half_to_f32<F16>(amax_bits16) / 127.0f;
 }
 
 // Quantisation of one value: round(fl32(x / s)) half to even, clamped to
@@ -71,11 +99,13 @@ __device__ __forceinline__ uint32_t clamp_pack4(float a, float b, float c, float
          ((uint32_t)id << 24);
 }
 
-// Quantises eight bf16 values (one 16-byte load) with scale s (r = 1/s) into
-// eight int8 packed little-endian in a uint2. A zero scale (all-zero row)
-// gives zeros. The division fallback is taken for the whole chunk, once per
-// wave, only when some lane has a value near a rounding boundary (or the
-// scale is subnormal), so the common path has no per-element branch.
+// Quantises eight bf16 (or fp16) values (one 16-byte load) with scale s
+// (r = 1/s) into eight int8 packed little-endian in a uint2. A zero scale
+// (all-zero row) gives zeros. The division fallback is taken for the whole
+// chunk, once per wave, only when some lane has a value near a rounding
+// boundary (or the scale is subnormal), so the common path has no
+// per-element branch.
+template <bool F16 = false>
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bool exact_div) {
   if (zero) return make_uint2(0u, 0u);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -83,8 +113,8 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bo
   bool any_near = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    x[2 * i] = half_to_f32<F16>(w[i] & 0xffffu);
+    x[2 * i + 1] = half_to_f32<F16>(w[i] >> 16);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -8,9 +8,9 @@
 
 namespace w8a8 {
 
-// Per-row symmetric int8 quantisation of R bf16 rows of length K.
+// Per-row symmetric int8 quantisation of R bf16 (f16: fp16) rows of length K.
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t K, int64_t ldx,
-                             int8_t* q, float* scale, hipStream_t stream);
+                             int8_t* q, float* scale, hipStream_t stream, bool f16 = false);
 
 struct GemmArgs {
   const int8_t* xq;        // [M, K]
@@ -21,6 +21,7 @@ struct GemmArgs {
   uint16_t* out;           // [M, ldo]
   int32_t* acc_debug;      // [M, N] or nullptr
   int64_t M, N, K, ldo;
+  bool f16 = false;        // bias, out (and the small-M kernel's x) are fp16, not bf16
 };
 
 // Bit 0: out rows allow 8-byte stores of four bf16 (out 8-byte aligned,
