@@ -314,41 +314,42 @@ def scale_to_f32(scale, dtype: str) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# W8A16: int8 weight-only with bf16 activations
+# W8A16: int8 weight-only with bf16 (or fp16) activations
 #
 # "Issue 5 probe ...", section "Round one: int8 weight-only via
 # compressed-tensors": int8 weight-only (W8A16), per-output-channel symmetric
-# weights, bf16 activations (no activation quantisation).
+# weights, bf16 activations (no activation quantisation); the round's
+# per-layer table runs the layers with bf16 and with fp16 activations.
 # Readings where the page is silent: the per-channel scale is applied once
 # to the sum, acc = sum_k fp32(x[k]) * wq[n,k] (each product is exact in
-# fp32: 8 x 8 significant bits), y = bf16_rne(fl32(fl32(acc) * s_w) +
-# fp32(bias)); the oracle takes acc in float64 (exact for inputs whose
-# products span fewer than 53 bits) and rounds it to fp32 once. A kernel that
+# fp32: 8 (bf16) or 11 (fp16) x 8 significant bits), y =
+# round_to_nearest_even(fl32(fl32(acc) * s_w) + fp32(bias)) in the type of x;
+# the oracle takes acc in float64 and rounds it to fp32 once. A kernel that
 # accumulates in fp32 differs from it by its accumulation error, bounded in
 # the parity test by a multiple of 2^-24 * sum_k |x[k] * wq[n,k]|.
 
-def w8a16_acc(x_bits, wq) -> np.ndarray:
-    """float64 sum_k x[m,k] * wq[n,k] for bf16 x [M,K] and int8 wq [N,K]."""
-    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+def w8a16_acc(x_bits, wq, dtype: str = "bf16") -> np.ndarray:
+    """float64 sum_k x[m,k] * wq[n,k] for x [M,K] (bf16 or fp16 bits) and int8 wq [N,K]."""
+    x = to_f32(x_bits, dtype).astype(np.float64)
     return x @ np.asarray(wq, np.float64).T
 
 
-def w8a16_abs_sum(x_bits, wq) -> np.ndarray:
+def w8a16_abs_sum(x_bits, wq, dtype: str = "bf16") -> np.ndarray:
     """sum_k |x[m,k] * wq[n,k]|, the scale of the accumulation error."""
-    x = np.abs(bf16_bits_to_f32(x_bits).astype(np.float64))
+    x = np.abs(to_f32(x_bits, dtype).astype(np.float64))
     return x @ np.abs(np.asarray(wq, np.float64)).T
 
 
-def w8a16_linear(x_bits, wq, s_w, bias_bits=None) -> dict:
-    """W8A16 linear: bf16 x [M,K], int8 wq [N,K], fp32 s_w [N] -> bf16 y bits.
+def w8a16_linear(x_bits, wq, s_w, bias_bits=None, dtype: str = "bf16") -> dict:
+    """W8A16 linear: x [M,K] (bf16, or fp16 with dtype='f16'), int8 wq [N,K],
+    fp32 s_w [N] -> y bits of the type of x (bias has that type too).
 
-    Returns acc (float64) and y (bf16 bits).
+    Returns acc (float64) and y.
     """
-    acc = w8a16_acc(x_bits, wq)
+    acc = w8a16_acc(x_bits, wq, dtype)
     t = acc.astype(np.float32)                                   # one RNE rounding
     t = t * np.asarray(s_w, dtype=np.float32)[None, :]
     if bias_bits is not None:
-        t = t + bf16_bits_to_f32(bias_bits)[None, :]
+        t = t + to_f32(bias_bits, dtype)[None, :]
     assert t.dtype == np.float32
-    return {"acc": acc, "y": f32_to_bf16_bits(t)}
-
+    return {"acc": acc, "y": from_f32(t, dtype)}

@@ -58,10 +58,10 @@ def pack_quantized_cases():
     return out
 
 
-def w8a16_cases():
+def w8a16_cases(name="w8a16_hand_cases.txt"):
     """[(x values, wq values, s_w, bias_bits or None, y_bits)]"""
     out = []
-    for line in _lines("w8a16_hand_cases.txt"):
+    for line in _lines(name):
         xs, ws, s, b, y = (p.strip() for p in line.split("|"))
         out.append(([_num(t) for t in xs.split()], [int(t) for t in ws.split()], _num(s),
                     None if b == "-" else int(b, 16), int(y, 16)))
