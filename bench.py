@@ -149,6 +149,7 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
     wq0, sw = w8.quantize_weights(to_dev(d["w"]))
     wqs = [wq0] + [wq0.clone() for _ in range(n_copies - 1)]
     bias, x = to_dev(d["bias"]), to_dev(d["x"])
+    bias16, x16 = bias.to(torch.float16), x.to(torch.float16)   # fp16 activations
     out = torch.empty((16, N), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((w8.workspace_bytes(16, K, N),), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -177,6 +178,9 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
         us16 = timed(lambda i: ok(lib.w8a16_linear(
             x.data_ptr(), M, K, K, wqs[i % n_copies].data_ptr(), sw.data_ptr(), N,
             bias.data_ptr(), out.data_ptr(), N, sp.cuda_stream)))
+        us16h = timed(lambda i: ok(lib.w8a16_linear_f16(
+            x16.data_ptr(), M, K, K, wqs[i % n_copies].data_ptr(), sw.data_ptr(), N,
+            bias16.data_ptr(), out.data_ptr(), N, sp.cuda_stream)))
         us8 = timed(lambda i: ok(lib.w8a8_linear(
             x.data_ptr(), M, K, K, wqs[i % n_copies].data_ptr(), sw.data_ptr(), N,
             bias.data_ptr(), out.data_ptr(), N, ws.data_ptr(), ws.numel(), None,
@@ -184,6 +188,7 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
         res["modulation"][f"M{M}"] = {
             "w8a16_us": us16, "w8a16_gbs": alg / (us16 * 1e-6) / 1e9,
             "w8a16_pct_hbm": 100 * alg / (us16 * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "w8a16_f16_us": us16h, "w8a16_f16_gbs": alg / (us16h * 1e-6) / 1e9,
             "w8a8_us": us8, "w8a8_gbs": alg / (us8 * 1e-6) / 1e9,
             "w8a8_pct_hbm": 100 * alg / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS}
     del wqs

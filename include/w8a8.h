@@ -199,6 +199,14 @@ int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int6
 int w8a16_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                  const int8_t* wq, const float* w_scale, int64_t N,
                  const uint16_t* bias, uint16_t* out, int64_t ldo, void* stream);
+/* The same with fp16 activations, bias and output (the probe's Round one ran
+ * the weight-only layers with bf16 and with fp16 activations):
+ *   y = fp16_rne(fl32(acc * w_scale[n]) + bias[n]), acc = sum_k fp32(x) * wq
+ * (every fp16 x int8 product is exact in fp32); subnormal results kept,
+ * overflow to +-inf. Requirements and errors as w8a16_linear. */
+int w8a16_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                     const int8_t* wq, const float* w_scale, int64_t N,
+                     const uint16_t* bias, uint16_t* out, int64_t ldo, void* stream);
 
 /* Workspace bytes w8a8_linear needs for this shape (0 if M == 0). */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);

@@ -14,8 +14,8 @@ import torch
 
 import oracle
 import w8a8_int8_dynamic_quant_amd as w8
-from gpu_util import announce, dev_bf16, host_bits
-from synth_inputs import make_linear_inputs, random_bf16, to_bf16_bits
+from gpu_util import announce, dev_bf16, dev_f16, host_bits
+from synth_inputs import make_linear_inputs, random_bf16, random_f16, to_bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -29,20 +29,24 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _ulp_bf16(v):
+def _ulp(v, dtype="bf16"):
+    """One ulp of the output type at |v| (bf16: 8 significant bits, smallest
+    subnormal 2^-133; fp16: 11 bits, 2^-24)."""
     v = np.abs(np.asarray(v, np.float64))
-    e = np.floor(np.log2(np.maximum(v, 2.0**-133)))
-    return np.maximum(2.0 ** (e - 7), 2.0**-133)
+    bits, tiny = (7, -133) if dtype == "bf16" else (10, -24)
+    e = np.floor(np.log2(np.maximum(v, 2.0**tiny)))
+    return np.maximum(2.0 ** (e - bits), 2.0**tiny)
 
 
-def check_w8a16(x_bits, wq, sw, bias_bits, y_bits) -> dict:
+def check_w8a16(x_bits, wq, sw, bias_bits, y_bits, dtype="bf16") -> dict:
     K = x_bits.shape[1]
-    exp = oracle.w8a16_linear(x_bits, wq, sw, bias_bits)
+    exp = oracle.w8a16_linear(x_bits, wq, sw, bias_bits, dtype)
     steps = 2 * ((K + 127) // 128) + 1
-    err = (2 * steps + 8) * 2.0**-24 * oracle.w8a16_abs_sum(x_bits, wq) * np.abs(sw)[None, :]
-    y = oracle.bf16_bits_to_f32(y_bits).astype(np.float64)
-    ye = oracle.bf16_bits_to_f32(exp["y"]).astype(np.float64)
-    tol = err + _ulp_bf16(np.maximum(np.abs(y), np.abs(ye)))
+    err = (2 * steps + 8) * 2.0**-24 * oracle.w8a16_abs_sum(x_bits, wq, dtype) * np.abs(sw)[None, :]
+    y = oracle.to_f32(y_bits, dtype).astype(np.float64)
+    ye = oracle.to_f32(exp["y"], dtype).astype(np.float64)
+    assert np.all(np.isfinite(ye)), "the cases stay inside the output range"
+    tol = err + _ulp(np.maximum(np.abs(y), np.abs(ye)), dtype)
     bad = np.abs(y - ye) > tol
     stats = {"n": int(y.size), "n_diff": int(np.count_nonzero(y_bits != exp["y"])),
              "max_excess": float(np.max(np.abs(y - ye) - tol)) if y.size else 0.0}
@@ -107,3 +111,62 @@ def test_w8a16_mixed_magnitudes():
     y = w8.w8a16_linear(dev_bf16(x), torch.from_numpy(wq).cuda(), torch.from_numpy(sw).cuda())
     torch.cuda.synchronize()
     print(check_w8a16(x, wq, sw, None, host_bits(y)))
+
+
+# ---- fp16 activations, bias and output (w8a16_linear_f16) -----------------
+
+@pytest.mark.parametrize("M,K,N", [(1, 16, 1), (3, 48, 70), (5, 1040, 129), (9, 512, 33),
+                                   (16, 3968, 100), (8, 8064, 24)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a16_f16_shapes(M, K, N, with_bias):
+    rng = np.random.default_rng(M * 11 + K + N)
+    x = random_f16(rng, (M, K))
+    w = random_f16(rng, (N, K), 0.02)
+    b = random_f16(rng, (N,), 0.01) if with_bias else None
+    wq_e, sw_e = oracle.quantize_weights(w, "f16")
+    wq, sw = w8.quantize_weights(dev_f16(w))
+    announce(f"w8a16 f16 M={M} K={K} N={N} bias={with_bias}")
+    y = w8.w8a16_linear(dev_f16(x), wq, sw, None if b is None else dev_f16(b))
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16
+    print(check_w8a16(x, wq_e, sw_e, b, host_bits(y), "f16"))
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_w8a16_f16_modulation_full_size(m):
+    rng = np.random.default_rng(31 + m)
+    x = random_f16(rng, (m, 3072))
+    w = random_f16(rng, (18432, 3072), 0.02)
+    b = random_f16(rng, (18432,), 0.01)
+    wq_e, sw_e = oracle.quantize_weights(w, "f16")
+    wq, sw = w8.quantize_weights(dev_f16(w))
+    announce(f"w8a16 f16 modulation M={m}")
+    y = w8.w8a16_linear(dev_f16(x), wq, sw, dev_f16(b))
+    torch.cuda.synchronize()
+    print(m, check_w8a16(x, wq_e, sw_e, b, host_bits(y), "f16"))
+
+
+def test_w8a16_f16_every_weight_value():
+    """Every int8 weight value -128..127 (the widening's whole domain, -128
+    included as ingest may produce it) against one-hot activations: the
+    outputs are the weights times the scale, exactly."""
+    K, N = 256, 16
+    wq = ((np.arange(N * K) % 256) - 128).astype(np.int8).reshape(N, K)
+    x = np.zeros((8, K), np.float64)
+    for t in range(8):
+        x[t, 37 * t % K] = 1.0
+    xb = to_f16_bits_exact(x)
+    sw = np.full(N, 0.5, np.float32)
+    announce("w8a16 f16 every weight value")
+    y = w8.w8a16_linear(dev_f16(xb), torch.from_numpy(wq).cuda(), torch.from_numpy(sw).cuda())
+    torch.cuda.synchronize()
+    got = oracle.f16_bits_to_f32(host_bits(y)).astype(np.float64)
+    want = np.stack([wq[:, 37 * t % K].astype(np.float64) * 0.5 for t in range(8)])
+    assert np.array_equal(got, want)
+
+
+def to_f16_bits_exact(a):
+    from synth_inputs import to_f16_bits
+    b = to_f16_bits(a)
+    assert np.array_equal(oracle.f16_bits_to_f32(b).astype(np.float64), a)
+    return b

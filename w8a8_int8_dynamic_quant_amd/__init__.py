@@ -50,6 +50,7 @@ SYMBOLS = (
     "w8a8_gemm_tile",
     "w8a8_unpack_pack_quantized",
     "w8a16_linear",
+    "w8a16_linear_f16",
     "w8a8_status_string",
     "w8a8_last_hip_error",
 )
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
     L.w8a8_gemm_tile.argtypes = [i64, i64, i64, ctypes.POINTER(ci), ctypes.POINTER(ci)]
     L.w8a8_unpack_pack_quantized.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
     L.w8a16_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp]
+    L.w8a16_linear_f16.argtypes = L.w8a16_linear.argtypes
     L.w8a8_status_string.argtypes = [ci]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
@@ -99,6 +101,7 @@ def lib() -> ctypes.CDLL:
                  "w8a8_quantize_weights_f16", "w8a8_quant_act_f16", "w8a8_scaled_mm_f16",
                  "w8a8_linear_f16",
                  "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized", "w8a16_linear",
+                 "w8a16_linear_f16",
                  "w8a8_last_hip_error"):
         getattr(L, name).restype = ci
     _lib = L
@@ -237,22 +240,22 @@ def unpack_pack_quantized(packed: torch.Tensor, scale: torch.Tensor):
 
 
 def w8a16_linear(x, wq, w_scale, bias=None, out=None):
-    """W8A16 linear for M <= 16: bf16 x [M, K] (not quantised) with int8
-    weights [N, K] and fp32 per-channel scales -> bf16 [M, N]."""
-    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    """W8A16 linear for M <= 16: bf16 (or fp16) x [M, K] (not quantised) with
+    int8 weights [N, K] and fp32 per-channel scales -> [M, N] of x's type."""
+    fn = "w8a16_linear" + _half(x.dtype, "x")
+    M, K, ldx = _rows(x, x.dtype, "x")
     N, K2, ldw = _rows(wq, torch.int8, "wq")
     if K2 != K or (N > 1 and ldw != K):
         raise ValueError("wq must be contiguous [N, K] with the K of x")
     _vec(w_scale, torch.float32, N, "w_scale")
-    _vec(bias, torch.bfloat16, N, "bias")
+    _vec(bias, x.dtype, N, "bias")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    Mo, No, ldo = _rows(out, torch.bfloat16, "out")
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    Mo, No, ldo = _rows(out, x.dtype, "out")
     if (Mo, No) != (M, N):
         raise ValueError("out must be [M, N]")
-    _check("w8a16_linear",
-           lib().w8a16_linear(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias), _ptr(out),
-                              ldo, _stream(x.device)))
+    _check(fn, getattr(lib(), fn)(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
+                                  _ptr(out), ldo, _stream(x.device)))
     return out
 
 

@@ -92,6 +92,20 @@ int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const in
   return hip_status(w8a8::launch_gemm(g, st));
 }
 
+int w8a16_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                 const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out, int64_t ldo,
+                 void* stream, bool f16) {
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, nullptr)) return s;
+  if (int s = check_bf16_ld(ldx, K)) return s;
+  if (M > W8A16_MAX_M || w8a8::w8a16_lds_bytes(M, K) > w8a8::kW8A16MaxLds)
+    return W8A8_ERR_UNSUPPORTED;
+  if (M == 0) return W8A8_OK;
+  if (!x) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
+  w8a8::GemmArgs g{nullptr, nullptr, wq, w_scale, bias, out, nullptr, M, N, K, ldo, f16};
+  return hip_status(w8a8::launch_w8a16(x, ldx, g, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,14 +202,13 @@ int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int6
 int w8a16_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
                  const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out, int64_t ldo,
                  void* stream) {
-  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, nullptr)) return s;
-  if (int s = check_bf16_ld(ldx, K)) return s;
-  if (M > W8A16_MAX_M || w8a8::w8a16_lds_bytes(M, K) > w8a8::kW8A16MaxLds) return W8A8_ERR_UNSUPPORTED;
-  if (M == 0) return W8A8_OK;
-  if (!x) return W8A8_ERR_INVALID_ARG;
-  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
-  w8a8::GemmArgs g{nullptr, nullptr, wq, w_scale, bias, out, nullptr, M, N, K, ldo};
-  return hip_status(w8a8::launch_w8a16(x, ldx, g, (hipStream_t)stream));
+  return w8a16_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, stream, false);
+}
+
+int w8a16_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                     const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
+                     int64_t ldo, void* stream) {
+  return w8a16_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, stream, true);
 }
 
 const char* w8a8_status_string(int status) {

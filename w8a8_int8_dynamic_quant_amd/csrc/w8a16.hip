@@ -1,5 +1,6 @@
 // W8A16 linear for M <= 16: int8 weights with fp32 per-output-channel scales,
-// bf16 activations used as they are (no activation quantisation) (gfx950).
+// bf16 (or fp16) activations used as they are (no activation quantisation)
+// (gfx950).
 //
 // The int8 weight-only scheme of the Issue 5 probe ("Round one: int8
 // weight-only via compressed-tensors"), for the small-M layers that stream
@@ -36,7 +37,9 @@ constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor boun
 constexpr int kD = 24;                   // 128-byte windows in flight per wave
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -66,11 +69,25 @@ __device__ __forceinline__ v8bf widen8(uint32_t lo, uint32_t hi) {
     // high halves of the two floats: bytes 2,3 of f0 then bytes 2,3 of f1
     o[i] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
   }
-  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
   return __builtin_bit_cast(v8bf, (v4u){o[0], o[1], o[2], o[3]});
 }
 
-template <bool HAS_BIAS, bool TWO, bool LONG>
+// Eight signed bytes (two words) -> eight fp16, exactly, with one byte
+// permute per pair: the biased byte u = q + 128 (q with its top bit flipped)
+// under the byte 0x64 is the fp16 value 1024 + u, and one packed fp16
+// subtraction of 1152 leaves q (every step exact: integers below 2048).
+__device__ __forceinline__ v8h widen8_f16(uint32_t lo, uint32_t hi) {
+  const uint32_t ulo = lo ^ 0x80808080u, uhi = hi ^ 0x80808080u;
+  // selector bytes 0-3 pick from the second operand, 4-7 from the first
+  const v4u o = {__builtin_amdgcn_perm(0x64646464u, ulo, 0x04010400u),
+                 __builtin_amdgcn_perm(0x64646464u, ulo, 0x04030402u),
+                 __builtin_amdgcn_perm(0x64646464u, uhi, 0x04010400u),
+                 __builtin_amdgcn_perm(0x64646464u, uhi, 0x04030402u)};
+  const _Float16 off = (_Float16)1152.0f;
+  return __builtin_bit_cast(v8h, o) - (v8h){off, off, off, off, off, off, off, off};
+}
+
+template <bool HAS_BIAS, bool TWO, bool LONG, bool F16>
 __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                     GemmArgs a, int vec_flags) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
@@ -125,12 +142,22 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
     const int wc = min(w, nwin - 1);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const v8bf A = widen8((uint32_t)wv[2 * e], (uint32_t)wv[2 * e + 1]);
-      const v8bf B0 = *reinterpret_cast<const v8bf*>(xb0 + 256 * wc + 16 * e);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
-      if constexpr (TWO) {
-        const v8bf B1 = *reinterpret_cast<const v8bf*>(xb1 + 256 * wc + 16 * e);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
+      if constexpr (F16) {
+        const v8h A = widen8_f16((uint32_t)wv[2 * e], (uint32_t)wv[2 * e + 1]);
+        const v8h B0 = *reinterpret_cast<const v8h*>(xb0 + 256 * wc + 16 * e);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B0, acc0, 0, 0, 0);
+        if constexpr (TWO) {
+          const v8h B1 = *reinterpret_cast<const v8h*>(xb1 + 256 * wc + 16 * e);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B1, acc1, 0, 0, 0);
+        }
+      } else {
+        const v8bf A = widen8((uint32_t)wv[2 * e], (uint32_t)wv[2 * e + 1]);
+        const v8bf B0 = *reinterpret_cast<const v8bf*>(xb0 + 256 * wc + 16 * e);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc0, 0, 0, 0);
+        if constexpr (TWO) {
+          const v8bf B1 = *reinterpret_cast<const v8bf*>(xb1 + 256 * wc + 16 * e);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc1, 0, 0, 0);
+        }
       }
     }
   };
@@ -169,7 +196,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
   for (int r = 0; r < 4; ++r) {
     const bool ok = nl + r < rows_valid;
     sw[r] = ok ? a.w_scale[n + r] : 0.f;
-    bb[r] = (HAS_BIAS && ok) ? bf16_to_f32(a.bias[n + r]) : 0.f;
+    bb[r] = (HAS_BIAS && ok) ? half_to_f32<F16>(a.bias[n + r]) : 0.f;
   }
 #pragma unroll
   for (int blk = 0; blk < (TWO ? 2 : 1); ++blk) {
@@ -182,7 +209,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
 #pragma clang fp contract(off)
       float t = c[r] * sw[r];
       if (HAS_BIAS) t = t + bb[r];
-      y[r] = f32_to_bf16_rne(t);
+      y[r] = f32_to_half_rne<F16>(t);
     }
     uint16_t* o = a.out + (int64_t)m * a.ldo + n;
     if (nl + 3 < rows_valid && (vec_flags & 1)) {
@@ -195,17 +222,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
   }
 }
 
-template <bool HAS_BIAS, bool TWO>
+template <bool HAS_BIAS, bool TWO, bool F16>
 hipError_t launch_w8a16_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, hipStream_t stream) {
   const RowGroupGrid g = row_group_grid(a.N);
   const dim3 grid(g.blocks), block(64 * g.waves);
   const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)w8a16_row_bytes(a.K);
   const int vf = epilogue_vec_flags(a);
   if (a.K > 128 * kD)
-    hipLaunchKernelGGL((w8a16_kernel<HAS_BIAS, TWO, true>), grid, block, lds, stream, x, ldx, a, vf);
+    hipLaunchKernelGGL((w8a16_kernel<HAS_BIAS, TWO, true, F16>), grid, block, lds, stream, x, ldx, a,
+                       vf);
   else
-    hipLaunchKernelGGL((w8a16_kernel<HAS_BIAS, TWO, false>), grid, block, lds, stream, x, ldx, a, vf);
+    hipLaunchKernelGGL((w8a16_kernel<HAS_BIAS, TWO, false, F16>), grid, block, lds, stream, x, ldx,
+                       a, vf);
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_w8a16_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a,
+                              hipStream_t stream) {
+  if (a.bias)
+    return a.M > 8 ? launch_w8a16_variant<true, true, F16>(x, ldx, a, stream)
+                   : launch_w8a16_variant<true, false, F16>(x, ldx, a, stream);
+  return a.M > 8 ? launch_w8a16_variant<false, true, F16>(x, ldx, a, stream)
+                 : launch_w8a16_variant<false, false, F16>(x, ldx, a, stream);
 }
 
 }  // namespace
@@ -216,11 +255,8 @@ size_t w8a16_lds_bytes(int64_t M, int64_t K) {
 
 hipError_t launch_w8a16(const uint16_t* x, int64_t ldx, const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  if (a.bias)
-    return a.M > 8 ? launch_w8a16_variant<true, true>(x, ldx, a, stream)
-                   : launch_w8a16_variant<true, false>(x, ldx, a, stream);
-  return a.M > 8 ? launch_w8a16_variant<false, true>(x, ldx, a, stream)
-                 : launch_w8a16_variant<false, false>(x, ldx, a, stream);
+  return a.f16 ? launch_w8a16_dtype<true>(x, ldx, a, stream)
+               : launch_w8a16_dtype<false>(x, ldx, a, stream);
 }
 
 }  // namespace w8a8
