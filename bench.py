@@ -16,6 +16,7 @@ GEMM launches (an event record costs GPU time); the full per-launch
 breakdown comes from a separate pass after it.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
+                    [--no-next-rows]
 """
 from __future__ import annotations
 
@@ -44,6 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip timing the CPU oracle (profiling runs)")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the W8A16 / ingest / fp16 measurements after the block step")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), the "
                         "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
@@ -423,8 +426,9 @@ def main():
                            f"{n_bd}-step pass after the timed region; gemm_us/gemm_tops and "
                            "roofline: events around the GEMM launches inside the timed region"),
     }
-    print("[bench] next rows (W8A16, ingest)", file=sys.stderr, flush=True)
-    line["next_rows"] = next_rows(w8, torch, np, dev, to_dev)
+    if not args.no_next_rows:
+        print("[bench] next rows (W8A16, ingest, fp16)", file=sys.stderr, flush=True)
+        line["next_rows"] = next_rows(w8, torch, np, dev, to_dev)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         import oracle
