@@ -43,13 +43,6 @@ namespace w8a8 {
 
 namespace {
 
-constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor bound
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
 // s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory ops (this wave's
 // newer panel loads) still in flight and every LDS read of this wave done.
 // gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in

@@ -40,7 +40,6 @@ namespace w8a8 {
 
 namespace {
 
-constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor bound
 constexpr int kD = 24;                   // 128-byte windows in flight per wave
 constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisation batch
 constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
@@ -51,16 +50,6 @@ constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight
 // windows refilled as they are consumed).
 enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
 // LDS row stride for the quantised activations: K rounded up to whole
 // 128-byte windows plus 32 bytes. One quarter-wave of the "B" read takes 8
 // tokens x 2 adjacent 16-byte chunks; with the stride an odd multiple of 32
@@ -68,14 +57,6 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // distinct 16-byte bank groups.
 __host__ __device__ inline int xs_stride(int64_t K) { return (int)((K + 127) / 128) * 128 + 32; }
 
-// Barrier on LDS traffic only (lgkmcnt 0, no fence): loads of weight windows
-// stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0); vmcnt and expcnt: no wait
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Quantises the row chunks held in v (chunk lane + 64*u of the row, u < kQ)
 // with the row's scale; returns the scale.

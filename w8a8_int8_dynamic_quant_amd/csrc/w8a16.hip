@@ -33,18 +33,12 @@ namespace w8a8 {
 
 namespace {
 
-constexpr uint32_t kOOB = 0x7ffffff0u;   // an offset past every descriptor bound
 constexpr int kD = 24;                   // 128-byte windows in flight per wave
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 // Bytes per LDS activation row: K bf16 rounded up to whole 128-element
 // windows, plus room for the per-token shift of w8a16_row_offset.

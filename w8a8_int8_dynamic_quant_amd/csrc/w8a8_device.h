@@ -18,10 +18,36 @@ namespace w8a8 {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-// 16-byte streaming load (non-temporal hint: the data is read once).
-__device__ __forceinline__ uint4 load_nt16(const void* p) {
-  const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+// An offset past every buffer descriptor bound: a load there reads zero, a
+// store there is dropped (used to mask lanes without branches).
+constexpr uint32_t kOOB = 0x7ffffff0u;
+
+// Raw buffer descriptor over `bytes` bytes from `base` (bounds-checked,
+// 32-bit offsets; loads past the bound return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16-byte buffer load.
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// 16-byte non-temporal buffer load (nt), for data read exactly once.
+__device__ __forceinline__ uint4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// Workgroup barrier on LDS traffic only (lgkmcnt 0, no fence): this wave's
+// outstanding global loads and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0); vmcnt and expcnt: no wait
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
