@@ -279,3 +279,20 @@ def test_linear_subnormal_scales_and_outputs():
         _, exp = _linear_case(x, w, None)
         y = oracle.bf16_bits_to_f32(exp["y"])
         assert np.any((np.abs(y) > 0) & (np.abs(y) < np.finfo(np.float32).tiny))
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040),
+                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088)])
+def test_linear_small_m_work_splits(M, N, K):
+    """Every way the small-M kernel splits the activation rows over its waves
+    (W = 4 waves for N = 70 and 200, 9 for N = 18432): one row per wave
+    (M <= W), two rows per wave held across the weight requests (W < M <=
+    2W), rows quantised before the stream (M > 2W) and rows longer than the
+    register-resident limit (K > 3072)."""
+    rng = np.random.default_rng(M * 31 + N + K)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    b = random_bf16(rng, (N,), 0.01)
+    announce(f"small-M work split M={M} N={N} K={K}")
+    assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
+    print(_linear_case(x, w, b)[0])

@@ -45,10 +45,11 @@ constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisa
 constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
 
 // Work split of a launch: ONE_ROW: M <= W and K <= kShortK (a wave quantises
-// at most one activation row, overlapped with the weight stream); SHORT:
-// K <= kShortK; LONG: longer rows (read twice for quantisation, weight
-// windows refilled as they are consumed).
-enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2 };
+// at most one activation row, overlapped with the weight stream); TWO_ROWS:
+// the same with up to two rows per wave (M <= 2W, bf16); SHORT: K <=
+// kShortK, rows quantised before the stream; LONG: longer rows (read twice
+// for quantisation, weight windows refilled as they are consumed).
+enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3 };
 
 // LDS row stride for the quantised activations: K rounded up to whole
 // 128-byte windows plus 32 bytes. One quarter-wave of the "B" read takes 8
@@ -162,14 +163,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   // ---- 1. activation quantisation into LDS, 2. weight requests ----
   // The K tail of each LDS row up to whole windows is never written: it only
   // meets weights that read as zero. Token rows >= M give unused columns.
-  if constexpr (MODE == ONE_ROW) {
-    uint4 v[kQ];
+  if constexpr (MODE == ONE_ROW || MODE == TWO_ROWS) {
+    // rows wave (and wave + W with TWO_ROWS) in registers across the weight
+    // requests
+    constexpr bool R2 = MODE == TWO_ROWS;
+    const int m2 = wave + W;
+    uint4 v[kQ], v2[R2 ? kQ : 1];
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)wave * ldx, (uint32_t)K * 2u);
     if (wave < M) {
 #pragma unroll
       for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0): this wave's row has arrived
+    if constexpr (R2) {
+      const __amdgpu_buffer_rsrc_t rx2 =
+          make_rsrc(x + (int64_t)(m2 < M ? m2 : 0) * ldx, m2 < M ? (uint32_t)K * 2u : 0u);
+#pragma unroll
+      for (int u = 0; u < kQ; ++u) v2[u] = load16(rx2, (uint32_t)(lane + 64 * u) * 16u);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0): this wave's rows have arrived
     __syncthreads();                       // ... and every other wave's
     issue_all();
     if (wave < M) {
@@ -178,6 +189,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
       if (lane == 0) {
         sa_lds[wave] = s;
         if (write_q) sa_out[wave] = s;
+      }
+    }
+    if constexpr (R2) {
+      if (m2 < M) {
+        const float s2 = quantise_regs<F16>(v2, nchunks, lane, xs + m2 * ldxs,
+                                            xq_out + (int64_t)m2 * K, write_q);
+        if (lane == 0) {
+          sa_lds[m2] = s2;
+          if (write_q) sa_out[m2] = s2;
+        }
       }
     }
     lds_barrier();
@@ -301,7 +322,12 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   else if (a.M <= g.waves)
     hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, ONE_ROW, F16>), grid, block, lds, stream, x,
                        ldx, a, xq_out, a_scale_out, vf);
-  else
+  else if (!F16 && a.M <= 2 * g.waves) {
+    // (bf16 only: the fp16 instantiation of this mode spills registers)
+    if constexpr (!F16)
+      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, TWO_ROWS, F16>), grid, block, lds, stream,
+                         x, ldx, a, xq_out, a_scale_out, vf);
+  } else
     hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT, F16>), grid, block, lds, stream, x, ldx,
                        a, xq_out, a_scale_out, vf);
   return hipGetLastError();
