@@ -246,7 +246,7 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not "
               "supported (the path shards by rows or columns with no communication; "
               "multi-GPU timing is out of scope)", file=sys.stderr)
         sys.exit(2)

@@ -71,7 +71,7 @@ typedef enum {
 
 /*
  * Load-time per-output-channel weight quantisation ("Int8 Quantization"
- * guide, "Overview": BF16/FP16 weights quantised at load time; Issue 5 probe,
+ * guide, "Overview": bf16 and fp16 weights quantised at load time; Issue 5 probe,
  * "Round two": unpacked int8 weights plus fp32 per-channel scales).
  *   w        [N, ldw] bf16 (read)
  *   wq       [N, K] int8, row stride K (written)
@@ -131,7 +131,7 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 #define W8A8_ALIGN256(b) ((((size_t)(b)) + 255u) & ~(size_t)255u)
 
 /*
- * fp16 variants ("Int8 Quantization" guide, "Overview": BF16/FP16 weights
+ * fp16 variants ("Int8 Quantization" guide, "Overview": bf16 and fp16 weights
  * are quantised at load time; Issue 5 probe, "Round one": the layers run with
  * bf16 and with fp16 activations). Each has the signature, layouts,
  * requirements and errors of the bf16 entry point of the same name, with
@@ -160,7 +160,7 @@ int w8a8_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
 /*
  * compressed-tensors pack-quantized ingest (Issue 5 probe, "Round one: int8
  * weight-only via compressed-tensors": weights stored with pack_to_int32, as
- * uint8 biased by 128, four per int32).
+ * unsigned bytes offset by 128, four to a 32-bit word).
  *   packed   [N, ldp] int32 (read); element 4i+j of a row is bits 8j..8j+7 of
  *            word i (little-endian), stored as q + 128
  *   scale_in [N] per-output-channel scale, type scale_dtype (W8A8_SCALE_F32,

@@ -23,7 +23,7 @@ Sources (page titles and sections; the pages are the authority):
   was that factor missing). Section "Kernel isolation": the reference the
   layer is compared against is float32 x @ dequant(W)^T.
 * "Int8 Quantization" (vLLM-Omni user guide), sections "Overview" and
-  "Parameters": BF16/FP16 weights are quantised at load time; only dynamic
+  "Parameters": bf16 and fp16 weights are quantised at load time; only dynamic
   (online) activation scaling exists.
 * "Qwen-Image-2.1: TE AutoRound-AWQ on GPU + all-resident single-3090 stack",
   section "Whole-pipeline follow-up": per-token activation and per-channel
@@ -36,7 +36,7 @@ the HIP path must reproduce):
 
 * scale = fl32(amax / 127) by one IEEE fp32 division; q = fl32(x / scale)
   by a second IEEE fp32 division, then round half to even, then clamp to
-  [-127, 127] ("symmetric": -128 is never produced).
+  [-127, 127] (symmetric: -128 is never produced).
 * all-zero row: scale = 0 and q = 0.
 * both scales are fp32.
 * epilogue order ((fl32(acc) * s_a) * s_w) + fp32(bias), each step rounded
@@ -46,8 +46,8 @@ the HIP path must reproduce):
   K <= 133 144.
 * subnormal inputs are legal and are not flushed; NaN/Inf inputs are outside
   the contract.
-* fp16 activations, weights, bias and output (the guide quantises "BF16/FP16"
-  weights; the Issue 5 probe, "Round one", runs bf16 and fp16 activations):
+* fp16 activations, weights, bias and output (the guide quantises bf16 and
+  fp16 weights; the Issue 5 probe, "Round one", runs bf16 and fp16 activations):
   the same maths with fp16 in place of bf16. Inputs convert exactly to fp32;
   y is the fp16 round to nearest even of the same fp32 value, and a value
   past the largest finite fp16 rounds to infinity as IEEE rounding does.
@@ -153,7 +153,7 @@ def quant_act(x_bits, dtype: str = "bf16") -> tuple[np.ndarray, np.ndarray]:
 
 def quantize_weights(w_bits, dtype: str = "bf16") -> tuple[np.ndarray, np.ndarray]:
     """Load-time per-output-channel quantisation of bf16 (or fp16) weights
-    [N,K] (Int8 Quantization guide, "Overview": quantise BF16/FP16 weights at
+    [N,K] (Int8 Quantization guide, "Overview": quantise bf16 and fp16 weights at
     load).
     """
     return quant_rows(to_f32(w_bits, dtype))
@@ -284,7 +284,7 @@ def rel_l2(a, b) -> float:
 #
 # "Issue 5 probe ...", section "Round one: int8 weight-only via
 # compressed-tensors": the int8 weight-only checkpoint stores its weights with
-# compressed-tensors' pack_to_int32, as uint8 biased by 128, four per int32,
+# compressed-tensors' pack_to_int32, as unsigned bytes offset by 128, four to a 32-bit word,
 # with a per-output-channel scale.
 # Readings where the page is silent: element 4i+j of a row sits in bits
 # 8j..8j+7 of word i (little-endian, first element in the low byte); the int8

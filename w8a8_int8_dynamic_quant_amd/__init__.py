@@ -220,7 +220,7 @@ _SCALE_DTYPES = {torch.float32: SCALE_F32, torch.bfloat16: SCALE_BF16, torch.flo
 def unpack_pack_quantized(packed: torch.Tensor, scale: torch.Tensor):
     """compressed-tensors pack-quantized weights -> (wq int8 [N, K], w_scale fp32 [N]).
 
-    packed: int32 [N, K/4] (uint8 biased by 128, four per word, little-endian);
+    packed: int32 [N, K/4] (bytes offset by 128, four to a word, little-endian);
     scale: fp32, bf16 or fp16 of N elements ([N] or [N, 1]).
     """
     N, words, ldp = _rows(packed, torch.int32, "packed")

@@ -1,8 +1,8 @@
 // compressed-tensors pack-quantized ingest: int32-packed weights -> int8 [N, K]
 // plus fp32 per-output-channel scales (gfx950).
 //
-// The pages' int8 weight-only checkpoint stores each weight as uint8 biased by
-// 128, four per int32 (Issue 5 probe, "Round one: int8 weight-only via
+// The pages' int8 weight-only checkpoint stores each weight as an unsigned byte
+// offset by 128, four to a 32-bit word (Issue 5 probe, "Round one: int8 weight-only via
 // compressed-tensors": the artifact is written with compressed-tensors'
 // pack_to_int32). Element 4i+j of a row sits in bits 8j..8j+7 of word i
 // (little-endian, the first element in the low byte), so the unpacked int8

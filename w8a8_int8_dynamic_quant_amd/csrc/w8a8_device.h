@@ -4,8 +4,8 @@
 // epilogue of the W8A8 int8-dynamic linear; Issue 5 probe, "Round two"):
 //   scale = fl32(amax / 127); q = clamp(rint(fl32(x / scale)), -127, 127)
 //   y = bf16_rne(((fl32(acc) * s_a) * s_w) + bias)
-// The same maths serves fp16 activations/weights/bias/output (the guide's
-// "BF16/FP16" weights): every helper that reads or writes 16-bit values takes
+// The same maths serves fp16 activations/weights/bias/output (the guide
+// quantises bf16 and fp16 weights): every helper that reads or writes 16-bit values takes
 // the type as a template flag (F16 = false: bf16).
 // Everything here is compiled with -ffp-contract=off so that no product and
 // sum are fused, and with IEEE (correctly rounded) fp32 division.

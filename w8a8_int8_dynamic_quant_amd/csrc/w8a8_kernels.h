@@ -54,7 +54,7 @@ hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a,
                           int8_t* xq_out, float* a_scale_out, hipStream_t stream);
 
 // compressed-tensors pack-quantized ingest: packed [N, ldp] int32 (uint8
-// biased by 128, four per word, little-endian) -> wq [N, K] int8, and scale_in
+// offset by 128, four to a word, little-endian) -> wq [N, K] int8, and scale_in
 // [N] (kScaleF32 / kScaleBF16 / kScaleF16) -> w_scale [N] fp32. K % 16 == 0,
 // ldp % 4 == 0, packed and wq 16-byte aligned.
 constexpr int kScaleF32 = 0, kScaleBF16 = 1, kScaleF16 = 2;
