@@ -11,24 +11,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace w8a8 {
 
 constexpr int kMinWaves = 4;    // waves per workgroup, lower bound
 constexpr int kMaxWaves = 12;   // 3 waves per SIMD: the kernels' register budget
 
-// Compute units of the current device (cached per device id).
+// Compute units of the current device, cached per device id (a device
+// property: threads that race on the first query store the same value).
 inline int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cus = 0;
+  int cus = cached[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus;
+    cached[dev].store(cus, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return cus;
 }
 
 struct RowGroupGrid {
