@@ -103,26 +103,40 @@ __device__ __forceinline__ float row_scale(uint32_t amax_bits16) {
 // 2^-15 from every half-integer, no rounding boundary lies between t and
 // fl32(Q) and rint(t) == rint(fl32(Q)). Otherwise (`near` is set) the caller
 // redoes the element with the IEEE division. (t - rint(t) is exact by
-// Sterbenz's lemma, so the distance test itself does not round.)
-__device__ __forceinline__ float quant_mul(float x, float r, bool& near) {
+// Sterbenz's lemma, so the distance test itself does not round.) The same
+// bound gives |t| < 127 (1 + 3u) < 127.5, so rint(t) needs no clamp.
+//
+// The rounding is the fp32 addition m = fl32(t + 1.5 * 2^23): every value
+// in [2^23, 2^24) is an integer, so m = 1.5 * 2^23 + rint(t) (round to
+// nearest even), rint(t) = m - 1.5 * 2^23 exactly, and the low byte of m's
+// bit pattern is rint(t) as a two's-complement int8. Returns m's bits.
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+
+__device__ __forceinline__ uint32_t quant_mul(float x, float r, bool& near) {
   const float t = x * r;
-  const float rt = __builtin_rintf(t);
-  const float d = __builtin_fabsf(t - rt);
-  near = __builtin_fabsf(0.5f - d) <= 0x1p-15f;
-  return rt;
+  const float m = t + kRoundMagic;
+  const float rt = m - kRoundMagic;
+  // |t - rint(t)| <= 1/2, so "within 2^-15 of a half-integer" is one compare
+  near = __builtin_fabsf(t - rt) >= 0.5f - 0x1p-15f;
+  return __float_as_uint(m);
 }
 
-// Exact route: one IEEE division. Used near rounding boundaries and for
-// rows whose scale is subnormal (1/s would overflow or lose precision).
-__device__ __forceinline__ float quant_div(float x, float s) { return __builtin_rintf(x / s); }
+// Exact route: one IEEE division, rounded half to even and clamped (a
+// subnormal scale can carry the quotient past 127.5). Used near rounding
+// boundaries and for rows whose scale is subnormal (1/s would overflow or
+// lose precision). Returns the int8 in the low byte.
+__device__ __forceinline__ uint32_t quant_div(float x, float s) {
+  return (uint32_t)(int)__builtin_amdgcn_fmed3f(__builtin_rintf(x / s), -127.0f, 127.0f);
+}
 
-__device__ __forceinline__ uint32_t clamp_pack4(float a, float b, float c, float d) {
-  const int ia = (int)__builtin_amdgcn_fmed3f(a, -127.0f, 127.0f);
-  const int ib = (int)__builtin_amdgcn_fmed3f(b, -127.0f, 127.0f);
-  const int ic = (int)__builtin_amdgcn_fmed3f(c, -127.0f, 127.0f);
-  const int id = (int)__builtin_amdgcn_fmed3f(d, -127.0f, 127.0f);
-  return (uint32_t)(ia & 0xff) | ((uint32_t)(ib & 0xff) << 8) | ((uint32_t)(ic & 0xff) << 16) |
-         ((uint32_t)id << 24);
+// Low bytes of four words, packed little-endian (a in byte 0).
+__device__ __forceinline__ uint32_t pack_low_bytes4(uint32_t a, uint32_t b, uint32_t c,
+                                                    uint32_t d) {
+  // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from
+  // the first, 12 gives zero
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
 }
 
 // Quantises eight bf16 (or fp16) values (one 16-byte load) with scale s
@@ -135,7 +149,8 @@ template <bool F16 = false>
 __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bool exact_div) {
   if (zero) return make_uint2(0u, 0u);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float x[8], q[8];
+  float x[8];
+  uint32_t q[8];
   bool any_near = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -156,7 +171,7 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bo
       if (near || exact_div) q[i] = quant_div(x[i], s);
     }
   }
-  return make_uint2(clamp_pack4(q[0], q[1], q[2], q[3]), clamp_pack4(q[4], q[5], q[6], q[7]));
+  return make_uint2(pack_low_bytes4(q[0], q[1], q[2], q[3]), pack_low_bytes4(q[4], q[5], q[6], q[7]));
 }
 
 __device__ __forceinline__ uint32_t absmax_bits8(uint4 v, uint32_t m) {
