@@ -13,9 +13,9 @@
 //  1. the M activation rows are quantised on chip (per-row amax, scale =
 //     amax/127, exact half-to-even rounding) into LDS as int8 [M][K];
 //     workgroup 0 also writes xq and a_scale out for the caller. The rows
-//     are read before any weight window is requested: vector-memory requests
-//     of the whole chip share the same queues, and the few KiB of x requested
-//     behind the weight stream would arrive last. With M <= W (at most one
+//     are requested before any weight window (vector-memory requests of the
+//     whole chip share the same queues, and the few KiB of x requested behind
+//     the weight stream would arrive last); the windows follow at once. With M <= W (at most one
 //     row per wave) the quantisation itself then runs while the weights
 //     stream;
 //  2. the wave requests up to kD 128-byte windows of its rows at once
@@ -180,9 +180,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int u = 0; u < kQ; ++u) v2[u] = load16(rx2, (uint32_t)(lane + 64 * u) * 16u);
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);    // vmcnt(0): this wave's rows have arrived
-    __syncthreads();                       // ... and every other wave's
+    // the weight requests go out right behind the row loads; vmcnt(kD) then
+    // waits for the rows only (loads complete in order)
+    __builtin_amdgcn_sched_barrier(0);
     issue_all();
+    wait_vmcnt<kD>();
     if (wave < M) {
       const float s = quantise_regs<F16>(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
                                     write_q);

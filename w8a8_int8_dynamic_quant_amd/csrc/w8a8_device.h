@@ -41,6 +41,15 @@ __device__ __forceinline__ uint4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t of
   return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
+// still in flight (expcnt, lgkmcnt: no wait). gfx9 encoding: vmcnt[3:0] in
+// bits 3:0 and vmcnt[5:4] in bits 15:14.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Workgroup barrier on LDS traffic only (lgkmcnt 0, no fence): this wave's
 // outstanding global loads and stores stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
