@@ -38,7 +38,8 @@
  *   is enqueued and an error status is returned (no exceptions, no abort).
  * - Requirements: M >= 0 (M == 0 is a no-op), N >= 1, 16 <= K <= W8A8_K_MAX
  *   and K % 16 == 0 (else W8A8_ERR_UNSUPPORTED); every leading dimension
- *   ld >= K (ldo >= N); bf16 input leading dimensions are multiples of 8;
+ *   ld >= K (ldo >= N, ldo <= W8A8_LDO_MAX); bf16 input leading dimensions
+ *   are multiples of 8;
  *   x/w/xq/wq/workspace pointers 16-byte aligned, scale/bias/out/acc_debug
  *   pointers 4-byte aligned (else W8A8_ERR_MISALIGNED).
  * - Outputs are undefined if an output buffer overlaps any other buffer.
@@ -68,6 +69,10 @@ typedef enum {
 #define W8A8_K_MAX 133144
 /* Rows up to this count take the small-M (weight-streaming) path. */
 #define W8A8_SMALL_M 16
+/* Largest output leading dimension (elements; the debug accumulators allow
+ * N up to half of it): kernels address a 256-row output tile with 32-bit
+ * byte offsets. Larger values give W8A8_ERR_UNSUPPORTED. */
+#define W8A8_LDO_MAX (1 << 22)
 
 /*
  * Load-time per-output-channel weight quantisation ("Int8 Quantization"

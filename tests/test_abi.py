@@ -36,6 +36,7 @@ def test_constants_match_header():
     text = open(HEADER).read()
     assert f"#define W8A8_K_MAX {w8.K_MAX}" in text
     assert f"#define W8A8_SMALL_M {w8.SMALL_M}" in text
+    assert "#define W8A8_LDO_MAX (1 << 22)" in text and w8.LDO_MAX == 1 << 22
     assert w8.K_MAX == (2**31 - 1) // (127 * 127)
 
 
@@ -91,6 +92,11 @@ def test_scaled_mm_validation(f):
     assert call(bias=P(A + 1)) == w8.ERR_MISALIGNED
     assert call(acc=P(A + 2)) == w8.ERR_MISALIGNED
     assert call(M=0, xq=None, sa=None, wq=None, sw=None, out=None) == w8.OK
+    # 32-bit tile addressing: ldo and, with debug accumulators, N are bounded
+    assert call(ldo=w8.LDO_MAX + 1) == w8.ERR_UNSUPPORTED
+    assert call(ldo=w8.LDO_MAX, acc=None, xq=None) == w8.ERR_INVALID_ARG   # ldo itself is fine
+    big = w8.LDO_MAX // 2 + 1
+    assert call(N=big, ldo=big, acc=P(A)) == w8.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("f", ["w8a8_linear", "w8a8_linear_f16"])

@@ -32,6 +32,7 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 K_MAX = 133144
 SMALL_M = 16
+LDO_MAX = 1 << 22
 PATH_NONE, PATH_SMALL_M, PATH_GEMM = 0, 1, 2
 SCALE_F32, SCALE_BF16, SCALE_F16 = 0, 1, 2
 W8A16_MAX_M = 16

@@ -47,6 +47,9 @@ int check_gemm(int64_t M, int64_t K, int64_t N, const int8_t* wq, const float* w
   if (M < 0 || N < 1) return W8A8_ERR_INVALID_ARG;
   if (int s = check_k(K)) return s;
   if (ldo < N) return W8A8_ERR_INVALID_ARG;
+  // a 256-row output tile (and the debug accumulators, row stride N) must be
+  // addressable with 32-bit byte offsets
+  if (ldo > W8A8_LDO_MAX || (acc_debug && N > W8A8_LDO_MAX / 2)) return W8A8_ERR_UNSUPPORTED;
   if (M == 0) return W8A8_OK;
   if (!wq || !w_scale || !out) return W8A8_ERR_INVALID_ARG;
   if (!aligned(wq, 16) || !aligned(w_scale, 4) || !aligned(out, 4)) return W8A8_ERR_MISALIGNED;
