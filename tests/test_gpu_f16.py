@@ -175,3 +175,16 @@ def test_f16_and_bf16_weights_interchangeable():
     torch.cuda.synchronize()
     exp = oracle.linear(xb, wq_e, sw_e, None, F16)
     assert_equal(host(acc), exp["acc"], "acc")
+
+
+@pytest.mark.parametrize("N", [512, 516, 514])
+def test_f16_256_tile_with_bias(N):
+    """fp16 bias and output through the 256x256 tile's three store paths."""
+    M, K = 520, 272
+    assert w8.gemm_tile(M, K, N) == (256, 256)
+    rng = np.random.default_rng(N + 77)
+    x = random_f16(rng, (M, K))
+    w = random_f16(rng, (N, K), 0.02)
+    b = random_f16(rng, (N,), 0.01)
+    announce(f"f16 256 tile M={M} N={N} K={K} bias")
+    print(_linear_case(x, w, b)[0])

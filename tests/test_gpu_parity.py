@@ -296,3 +296,19 @@ def test_linear_small_m_work_splits(M, N, K):
     announce(f"small-M work split M={M} N={N} K={K}")
     assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
     print(_linear_case(x, w, b)[0])
+
+
+@pytest.mark.parametrize("N", [512, 516, 514])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_256_tile_store_paths(N, with_bias):
+    """The 256x256 tile with each output store path: 16-byte rows staged in
+    LDS (N % 8 == 0), 8-byte stores (N % 4 == 0) and 2-byte stores, with and
+    without bias."""
+    M, K = 520, 272
+    assert w8.gemm_tile(M, K, N) == (256, 256)
+    rng = np.random.default_rng(N * 3 + with_bias)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    b = random_bf16(rng, (N,), 0.01) if with_bias else None
+    announce(f"256 tile store path M={M} N={N} K={K} bias={with_bias}")
+    print(_linear_case(x, w, b)[0])
