@@ -32,4 +32,13 @@ from .w8a8_oracle import (  # noqa: F401
     w8a16_acc,
     w8a16_abs_sum,
     w8a16_linear,
+    f64_to_bf16_bits,
+    layernorm_modulate,
+    gelu,
+    producer_quant,
+    layernorm_modulate_quant,
+    gelu_quant,
+    layernorm_modulate_err_bound,
+    gelu_err_bound,
+    bf16_within,
 )

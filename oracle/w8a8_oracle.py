@@ -13,6 +13,9 @@ weights W [N,K]):
   3. an int8 x int8 product with exact integer accumulation, stored as int32,
   4. an fp32 epilogue acc * act_scale * weight_scale (+ bias) rounded to bf16.
 
+and, for the producers fused with step 1, the modulated LayerNorm and the GELU
+whose bf16 output is quantised in the same pass (the last section).
+
 Sources (page titles and sections; the pages are the authority):
 
 * "Issue 5 probe: int8 quantized DiT serve paths on the RTX 3090 (24 GB)",
@@ -30,6 +33,9 @@ Sources (page titles and sections; the pages are the authority):
   weight quantisation.
 * unsloth commit log of test_diffusion_transformer_quant.py: int8 matmuls run
   with int32 accumulation.
+* "Qwen-Image-2.1 ...", section "Whole-pipeline follow-up": fused
+  activation-quantisation, normalisation and activation kernels around the
+  int8 GEMMs (the producers of the last section).
 
 Readings where the pages are silent (each is a choice this oracle fixes and
 the HIP path must reproduce):
@@ -54,8 +60,10 @@ the HIP path must reproduce):
 
 Parity pins: every function here is checked by tests that do not call it
 back (hand-computed golden files, exact rational arithmetic, brute force,
-closed forms, invariants, a library cast, and the pages' 0.17% figure).
-No function is "parity unpinned".
+closed forms, invariants, a library cast, the pages' 0.17% figure, and for
+the producers the standard normal table and independent library
+implementations of LayerNorm, GELU and erfc). No function is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -353,3 +361,194 @@ def w8a16_linear(x_bits, wq, s_w, bias_bits=None, dtype: str = "bf16") -> dict:
         t = t + to_f32(bias_bits, dtype)[None, :]
     assert t.dtype == np.float32
     return {"acc": acc, "y": from_f32(t, dtype)}
+
+
+# --------------------------------------------------------------------------
+# Producer fusion: the normalisation and the activation that produce a
+# linear's input, writing its int8 codes and per-row scales directly
+#
+# "Qwen-Image-2.1: TE AutoRound-AWQ on GPU + all-resident single-3090 stack",
+# section "Whole-pipeline follow-up": the W8A8 DiT path's kernel trace holds
+# the int8 GEMMs plus fused activation-quantisation, normalisation and
+# activation kernels around them. The page names those kernels, not their
+# formulas. Readings taken here:
+#
+# * the normalisation is the adaptive (modulated) LayerNorm in front of a DiT
+#   block's QKV and FFN-up linears: per row, the mean and the biased variance
+#   over K, then v = (x - mean) / sqrt(var + eps) * (1 + scale) + shift, with
+#   shift and scale bf16 vectors [K] shared by a group of rows (the tokens of
+#   one sample) and no learnt affine of its own;
+# * the activation is GELU in front of FFN-down: z * Phi(z), Phi the standard
+#   normal distribution function ("erf" form), or its tanh approximation
+#   0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)));
+# * the fused kernel computes what the unfused producer would write, v
+#   rounded to bf16 (nearest, ties to even), and quantises that bf16 row
+#   exactly as quant_act does.
+#
+# The oracle takes v in float64 and rounds it to bf16 once. A kernel that
+# evaluates v in fp32 is off by its rounding error; the *_err_bound functions
+# bound that error, and the parity tests allow it on top of bf16's own half
+# ulp. The int8 codes and scales are compared bit for bit after quantising
+# the kernel's own bf16 row, so both sides take the integer decisions on the
+# same bf16 values.
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    """float64 -> bf16 bit patterns with a single round to nearest even.
+
+    Rounding to fp32 first and then to bf16 can round twice the wrong way (a
+    value just above a bf16 midpoint can land on it in fp32). The first step
+    therefore rounds to odd: truncate toward zero to fp32, then set the last
+    bit if anything was dropped. With 16 more bits than bf16 that keeps every
+    later tie decision exact. Subnormals are kept; past the bf16 range the
+    result is infinity.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        f = v.astype(np.float32)
+    back = f.astype(np.float64)
+    bits = f.view(np.uint32).copy()
+    inexact = back != v
+    # magnitude one fp32 step toward zero where the nearest rounding went up
+    # (sign-magnitude patterns: decrementing the pattern shrinks |f|)
+    bits[inexact & (np.abs(back) > np.abs(v))] -= np.uint32(1)
+    bits[inexact] |= np.uint32(1)
+    return f32_to_bf16_bits(bits.view(np.float32))
+
+
+def _mod_rows(M: int, rows_per_group):
+    rpg = M if rows_per_group is None else int(rows_per_group)
+    if rpg < 1:
+        raise ValueError("rows_per_group must be >= 1")
+    return np.arange(M) // rpg
+
+
+def layernorm_modulate(x_bits, shift_bits, scale_bits, eps: float, rows_per_group=None):
+    """float64 v [M,K] of the modulated LayerNorm of bf16 rows x [M,K].
+
+    shift, scale: bf16 [G,K]; row m uses group m // rows_per_group (one
+    group for all rows when rows_per_group is None). eps is taken as the
+    fp32 value the kernel receives.
+    """
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    M, K = x.shape
+    g = _mod_rows(M, rows_per_group)
+    sh = bf16_bits_to_f32(np.atleast_2d(shift_bits)).astype(np.float64)
+    sc = bf16_bits_to_f32(np.atleast_2d(scale_bits)).astype(np.float64)
+    mean = x.mean(axis=1, keepdims=True)
+    d = x - mean
+    var = (d * d).mean(axis=1, keepdims=True)
+    e = float(np.float32(eps))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return d / np.sqrt(var + e) * (1.0 + sc[g]) + sh[g]
+
+
+def gelu(z_bits, approximate: str = "none") -> np.ndarray:
+    """float64 GELU of bf16 z: z * Phi(z) ('none') or the tanh form ('tanh').
+
+    Phi(z) = erfc(-z / sqrt 2) / 2 (no cancellation for z << 0). The tanh
+    form is evaluated through 0.5 (1 + tanh t) = 1 / (1 + exp(-2t)), which
+    is the same function without the cancellation of 1 + tanh(t) at t << 0.
+    """
+    from scipy.special import erfc
+    z = bf16_bits_to_f32(z_bits).astype(np.float64)
+    if approximate == "none":
+        return 0.5 * z * erfc(-z / np.sqrt(2.0))
+    if approximate == "tanh":
+        t = np.sqrt(2.0 / np.pi) * (z + 0.044715 * z * z * z)
+        with np.errstate(over="ignore"):
+            return z / (1.0 + np.exp(-2.0 * t))
+    raise ValueError(approximate)
+
+
+def producer_quant(v) -> dict:
+    """bf16 row values of the producer (nearest to v) and their quantisation."""
+    y = f64_to_bf16_bits(v)
+    xq, s = quant_act(y)
+    return {"y": y, "xq": xq, "a_scale": s}
+
+
+def layernorm_modulate_quant(x_bits, shift_bits, scale_bits, eps: float,
+                             rows_per_group=None) -> dict:
+    return producer_quant(layernorm_modulate(x_bits, shift_bits, scale_bits, eps,
+                                             rows_per_group))
+
+
+def gelu_quant(z_bits, approximate: str = "none") -> dict:
+    return producer_quant(gelu(z_bits, approximate))
+
+
+_U32 = 2.0 ** -24
+
+
+def layernorm_modulate_err_bound(x_bits, shift_bits, scale_bits, eps: float,
+                                 rows_per_group=None, depth=None) -> np.ndarray:
+    """Bound on |v32 - v| for an fp32 evaluation v32 of the modulated LayerNorm
+    (u = 2^-24, first order, doubled). depth is the longest chain of fp32
+    additions any term of the two row sums passes through: K - 1 when the
+    order is unknown (the default), less for a blocked or tree reduction.
+
+      mean:  |mean32 - mean| <= (depth + 1) u m1          (m1 = mean |x|)
+      d = x - mean32: off by that plus u |d|
+      var:   relative error <= (depth + 2) u, plus (mean32 - mean)^2 / var
+      rstd = 1 / sqrt(var + eps): relative error <= (depth + 3) u / 2 + 2 u
+      (1 + scale), the two products and the sum with shift: 4 u in all
+    so |v32 - v| <= (depth + 1) u m1 rstd |g| + (depth / 2 + 8) u |A|
+                    + u |shift| + (dm)^2 |A| / 2,
+    with A = (x - mean) rstd g and dm = (depth + 1) u m1 rstd.
+    """
+    x = bf16_bits_to_f32(x_bits).astype(np.float64)
+    M, K = x.shape
+    D = (K - 1) if depth is None else int(depth)
+    g = _mod_rows(M, rows_per_group)
+    sh = bf16_bits_to_f32(np.atleast_2d(shift_bits)).astype(np.float64)[g]
+    gain = 1.0 + bf16_bits_to_f32(np.atleast_2d(scale_bits)).astype(np.float64)[g]
+    mean = x.mean(axis=1, keepdims=True)
+    d = x - mean
+    rstd = 1.0 / np.sqrt((d * d).mean(axis=1, keepdims=True) + float(np.float32(eps)))
+    m1 = np.abs(x).mean(axis=1, keepdims=True)
+    a = np.abs(d * rstd * gain)
+    dm = (D + 1) * _U32 * m1 * rstd
+    e = dm * np.abs(gain) + (D / 2 + 8) * _U32 * a + _U32 * np.abs(sh) + 0.5 * dm * dm * a
+    return 2.0 * e + 2.0 ** -145
+
+
+def gelu_err_bound(z_bits, approximate: str = "none") -> np.ndarray:
+    """Bound on |v32 - v| for an fp32 evaluation of GELU by the forms above with
+    the fp32 library erfc / exp (each within 16 u of its result), doubled:
+
+      'none': the argument a = z / sqrt 2 carries 2 u, which erfc magnifies
+              by its condition number, at most 3 a^2 + 2; the library 16 u;
+              the two products 2 u:  (6 a^2 + 22) u |v|.
+      'tanh': t = sqrt(2/pi) (z + 0.044715 z^3) carries 8 u, e = exp(-2|t|)
+              magnifies it by 2|t|; the library 16 u; 1 + e and the
+              division 2 u:  (16 |t| + 20) u |v|. (An fp32 evaluation takes
+              z / (1 + e) for t >= 0 and z e / (1 + e) for t < 0: exp(-2t)
+              itself overflows for t < -44 while v is still an fp32 normal.)
+    Plus 2^-144 for results and intermediates in the fp32 subnormal range.
+    """
+    z = bf16_bits_to_f32(z_bits).astype(np.float64)
+    v = np.abs(gelu(z_bits, approximate))
+    if approximate == "none":
+        a = z / np.sqrt(2.0)
+        rel = (6.0 * a * a + 22.0) * _U32
+    elif approximate == "tanh":
+        t = np.sqrt(2.0 / np.pi) * (z + 0.044715 * z * z * z)
+        rel = (16.0 * np.abs(t) + 20.0) * _U32
+    else:
+        raise ValueError(approximate)
+    return 2.0 * rel * v + 2.0 ** -144
+
+
+def bf16_within(y_bits, v, err) -> np.ndarray:
+    """True where the bf16 value y is a correct result for the exact v when
+    the evaluation may be off by err: |y - v| <= half a bf16 ulp at v + err
+    (at a binade edge, half an ulp of the binade below). Infinite y is
+    accepted only where v is past the bf16 overflow threshold."""
+    y = bf16_bits_to_f32(y_bits).astype(np.float64)
+    v = np.asarray(v, np.float64)
+    av = np.abs(v)
+    e = np.frexp(np.maximum(av, 2.0 ** -126))[1] - 1         # exact binade of |v|
+    half_ulp = np.ldexp(1.0, e - 8)
+    ok = np.abs(y - v) <= half_ulp + err
+    big = av + err >= (2.0 - 2.0 ** -8) * 2.0 ** 127
+    return np.where(np.isinf(y), big & (np.sign(y) == np.sign(v)), ok)

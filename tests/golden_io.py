@@ -84,3 +84,19 @@ def f16_cases():
             out["epi"].append((int(acc), _num(sa), _num(sw), None if b == "-" else int(b, 16),
                                int(y, 16)))
     return out
+
+
+def producer_cases():
+    """(LN cases [(x, shift, scale, eps, v, q or None)], GELU cases [(z, Phi(z))])"""
+    ln, ge = [], []
+    for line in _lines("producer_hand_cases.txt"):
+        parts = [p.strip() for p in line.split("|")]
+        if parts[0] == "LN":
+            x, sh, sc, eps, v = ([_num(t) for t in p.split()] for p in parts[1:6])
+            q = [int(t) for t in parts[6].split()] if len(parts) > 6 else None
+            ln.append((x, sh, sc, eps[0], v, q))
+        elif parts[0] == "GELU":
+            ge.append((_num(parts[1]), _num(parts[2])))
+        else:
+            raise ValueError(line)
+    return ln, ge
