@@ -213,6 +213,62 @@ int w8a16_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                      const int8_t* wq, const float* w_scale, int64_t N,
                      const uint16_t* bias, uint16_t* out, int64_t ldo, void* stream);
 
+/*
+ * Producers fused with the activation quantisation ("Qwen-Image-2.1: TE
+ * AutoRound-AWQ on GPU + all-resident single-3090 stack", section
+ * "Whole-pipeline follow-up": the W8A8 DiT path runs fused
+ * activation-quantisation, normalisation and activation kernels around its
+ * int8 GEMMs). Each computes the producer's bf16 row y in registers and
+ * writes the per-row quantisation of y, bit for bit what w8a8_quant_act
+ * writes for y, without a bf16 round trip through memory. y itself is also
+ * written when a y pointer is given (else pass NULL; ldy is then ignored).
+ *   xq      [M, K] int8, row stride K (written)
+ *   a_scale [M] fp32 (written)
+ *   y       [M, ldy] bf16 (written) or NULL
+ * y is the fp32 evaluation of the formula rounded to bf16 (nearest even):
+ * within half a bf16 ulp of the exact value plus the fp32 rounding error.
+ * Requirements as w8a8_quant_act (16 <= K, K % 16 == 0, ld >= K and
+ * ld % 8 == 0, x / xq / y 16-byte aligned, a_scale 4-byte aligned), plus
+ * the per-producer limits below; ldy follows the rules of ldx when y is
+ * given. No workspace.
+ */
+
+/*
+ * Modulated (adaptive) LayerNorm, the normalisation in front of a DiT
+ * block's QKV and FFN-up linears:
+ *   y[m,k] = bf16((x[m,k] - mean_m) / sqrt(var_m + eps) * (1 + scale[g,k]) + shift[g,k])
+ * mean_m and the biased variance var_m over row m of x; g = m / rows_per_group
+ * (the tokens of one sample share a group's shift and scale).
+ *   x            [M, ldx] bf16 (read)
+ *   shift, scale [G, ld_mod] bf16 (read), G = ceil(M / rows_per_group)
+ * fp32 evaluation: every term of the two row sums passes through at most
+ * K / 64 + 16 additions; mean = sum / K, rstd = 1 / sqrt(var + eps).
+ * Limits: K <= 16384 (else W8A8_ERR_UNSUPPORTED); eps > 0 and finite,
+ * rows_per_group >= 1, ld_mod >= K (else W8A8_ERR_INVALID_ARG); ld_mod % 8
+ * == 0 (else W8A8_ERR_UNSUPPORTED); shift and scale 16-byte aligned.
+ */
+int w8a8_layernorm_modulate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const uint16_t* shift, const uint16_t* scale,
+                                      int64_t ld_mod, int64_t rows_per_group, float eps,
+                                      int8_t* xq, float* a_scale, uint16_t* y, int64_t ldy,
+                                      void* stream);
+
+/*
+ * GELU, the activation in front of a DiT block's FFN-down linear:
+ *   W8A8_GELU_ERF:  y = bf16(z Phi(z)), Phi the standard normal distribution
+ *                   function, evaluated as (0.5 z) erfc(-z / sqrt 2);
+ *   W8A8_GELU_TANH: y = bf16(0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))),
+ *                   evaluated as z / (1 + e) (t >= 0) or z e / (1 + e) (t < 0),
+ *                   e = exp(-2|t|), t the tanh argument.
+ *   z [M, ldz] bf16 (read)
+ * Limits: K <= 32768 (else W8A8_ERR_UNSUPPORTED); approximate one of the two
+ * values (else W8A8_ERR_INVALID_ARG).
+ */
+#define W8A8_GELU_ERF 0
+#define W8A8_GELU_TANH 1
+int w8a8_gelu_quant_act(const uint16_t* z, int64_t M, int64_t K, int64_t ldz, int approximate,
+                        int8_t* xq, float* a_scale, uint16_t* y, int64_t ldy, void* stream);
+
 /* Workspace bytes w8a8_linear needs for this shape (0 if M == 0). */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N);
 

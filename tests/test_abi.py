@@ -197,6 +197,73 @@ def test_w8a16_validation():
     assert f"#define W8A16_MAX_M {w8.W8A16_MAX_M}" in open(HEADER).read()
 
 
+def test_layernorm_modulate_validation():
+    f = "w8a8_layernorm_modulate_quant_act"
+    names = ["x", "M", "K", "ldx", "sh", "sc", "ldm", "rpg", "eps", "xq", "sa", "y", "ldy", "st"]
+    base = [P(A), 4, 3072, 3072, P(A), P(A), 3072, 4, ctypes.c_float(1e-6), P(A), P(A), None, 0,
+            None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = ctypes.c_float(v) if k == "eps" else v
+        return q(f, *a)
+
+    assert call(M=-1) == w8.ERR_INVALID_ARG
+    assert call(K=16400, ldx=16400, ldm=16400) == w8.ERR_UNSUPPORTED    # past the LN limit
+    assert call(K=40, ldx=40, ldm=40) == w8.ERR_UNSUPPORTED
+    assert call(ldx=3000) == w8.ERR_INVALID_ARG
+    assert call(ldx=3076) == w8.ERR_UNSUPPORTED
+    assert call(ldm=3064) == w8.ERR_INVALID_ARG
+    assert call(ldm=3076) == w8.ERR_UNSUPPORTED
+    assert call(rpg=0) == w8.ERR_INVALID_ARG
+    for eps in (0.0, -1e-6, float("inf"), float("nan")):
+        assert call(eps=eps) == w8.ERR_INVALID_ARG, eps
+    assert call(y=P(A), ldy=3000) == w8.ERR_INVALID_ARG
+    assert call(y=P(A), ldy=3076) == w8.ERR_UNSUPPORTED
+    for k in ("x", "sh", "sc", "xq", "sa"):
+        assert call(**{k: None}) == w8.ERR_INVALID_ARG, k
+    for k in ("x", "sh", "sc", "xq", "y"):
+        kw = {k: P(A + 8)}
+        if k == "y":
+            kw["ldy"] = 3072
+        assert call(**kw) == w8.ERR_MISALIGNED, k
+    assert call(sa=P(A + 2)) == w8.ERR_MISALIGNED
+    assert call(M=0, x=None, sh=None, sc=None, xq=None, sa=None) == w8.OK
+    assert w8.PRODUCER_MAX_K["layernorm"] == 16384
+
+
+def test_gelu_validation():
+    f = "w8a8_gelu_quant_act"
+    names = ["z", "M", "K", "ldz", "approx", "xq", "sa", "y", "ldy", "st"]
+    base = [P(A), 4, 12288, 12288, 0, P(A), P(A), None, 0, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(approx=2) == w8.ERR_INVALID_ARG
+    assert call(approx=-1) == w8.ERR_INVALID_ARG
+    assert call(M=-1) == w8.ERR_INVALID_ARG
+    assert call(K=32784, ldz=32784) == w8.ERR_UNSUPPORTED
+    assert call(K=24, ldz=24) == w8.ERR_UNSUPPORTED
+    assert call(ldz=12280) == w8.ERR_INVALID_ARG
+    assert call(ldz=12292) == w8.ERR_UNSUPPORTED
+    assert call(y=P(A), ldy=12280) == w8.ERR_INVALID_ARG
+    for k in ("z", "xq", "sa"):
+        assert call(**{k: None}) == w8.ERR_INVALID_ARG, k
+    assert call(z=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(xq=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(y=P(A + 8), ldy=12288) == w8.ERR_MISALIGNED
+    assert call(M=0, z=None, xq=None, sa=None) == w8.OK
+    text = open(HEADER).read()
+    assert f"#define W8A8_GELU_ERF {w8.GELU_ERF}" in text
+    assert f"#define W8A8_GELU_TANH {w8.GELU_TANH}" in text
+    assert w8.PRODUCER_MAX_K["gelu"] == 32768
+
+
 def test_status_strings():
     for s in (w8.OK, w8.ERR_INVALID_ARG, w8.ERR_UNSUPPORTED, w8.ERR_MISALIGNED,
               w8.ERR_WORKSPACE, w8.ERR_HIP):

@@ -13,6 +13,8 @@ there is no fallback.
     y = scaled_mm(xq, a_scale, wq, w_scale, bias)
     wq, w_scale = unpack_pack_quantized(packed, scale)  # compressed-tensors ingest
     y = w8a16_linear(x, wq, w_scale, bias)         # weight-only, M <= 16
+    xq, a_scale = layernorm_modulate_quant_act(x, shift, scale)  # fused producers
+    xq, a_scale = gelu_quant_act(z)
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ LDO_MAX = 1 << 22
 PATH_NONE, PATH_SMALL_M, PATH_GEMM = 0, 1, 2
 SCALE_F32, SCALE_BF16, SCALE_F16 = 0, 1, 2
 W8A16_MAX_M = 16
+GELU_ERF, GELU_TANH = 0, 1
+PRODUCER_MAX_K = {"layernorm": 16384, "gelu": 32768}
 
 SYMBOLS = (
     "w8a8_quantize_weights",
@@ -52,6 +56,8 @@ SYMBOLS = (
     "w8a8_unpack_pack_quantized",
     "w8a16_linear",
     "w8a16_linear_f16",
+    "w8a8_layernorm_modulate_quant_act",
+    "w8a8_gelu_quant_act",
     "w8a8_status_string",
     "w8a8_last_hip_error",
 )
@@ -95,6 +101,9 @@ def lib() -> ctypes.CDLL:
     L.w8a8_unpack_pack_quantized.argtypes = [vp, i64, i64, i64, vp, ci, vp, vp, vp]
     L.w8a16_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp]
     L.w8a16_linear_f16.argtypes = L.w8a16_linear.argtypes
+    L.w8a8_layernorm_modulate_quant_act.argtypes = [vp, i64, i64, i64, vp, vp, i64, i64,
+                                                    ctypes.c_float, vp, vp, vp, i64, vp]
+    L.w8a8_gelu_quant_act.argtypes = [vp, i64, i64, i64, ci, vp, vp, vp, i64, vp]
     L.w8a8_status_string.argtypes = [ci]
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
@@ -102,7 +111,7 @@ def lib() -> ctypes.CDLL:
                  "w8a8_quantize_weights_f16", "w8a8_quant_act_f16", "w8a8_scaled_mm_f16",
                  "w8a8_linear_f16",
                  "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized", "w8a16_linear",
-                 "w8a16_linear_f16",
+                 "w8a16_linear_f16", "w8a8_layernorm_modulate_quant_act", "w8a8_gelu_quant_act",
                  "w8a8_last_hip_error"):
         getattr(L, name).restype = ci
     _lib = L
@@ -313,3 +322,58 @@ def linear(x, wq, w_scale, bias=None, out=None, workspace=None, acc_debug=None):
                                   _ptr(out), ldo, _ptr(workspace), workspace.numel(),
                                   _ptr(acc_debug), _stream(x.device)))
     return out
+
+
+def _producer_out(x, M, K, return_y):
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    s = torch.empty((M,), dtype=torch.float32, device=x.device)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if return_y else None
+    return xq, s, y
+
+
+def layernorm_modulate_quant_act(x, shift, scale, eps: float = 1e-6, rows_per_group=None,
+                                 return_y: bool = False):
+    """Modulated LayerNorm of bf16 x [M, K] fused with its per-row int8
+    quantisation: (x - mean) / sqrt(var + eps) * (1 + scale) + shift, rounded
+    to bf16, then quantised -> (xq int8 [M, K], a_scale fp32 [M][, y bf16]).
+
+    shift, scale: bf16 [K] (every row) or [G, K] with the same row stride
+    (e.g. chunks of a modulation projection's output); row m uses group
+    m // rows_per_group (default: M / G, which must then divide evenly).
+    """
+    M, K, ldx = _rows(x, torch.bfloat16, "x")
+    if shift.dim() == 1:
+        shift, scale = shift.unsqueeze(0), scale.unsqueeze(0)
+    G, Ks, ldm = _rows(shift, torch.bfloat16, "shift")
+    G2, Kc, ldm2 = _rows(scale, torch.bfloat16, "scale")
+    if (G2, Kc) != (G, Ks) or Ks != K:
+        raise ValueError("shift and scale must both be [K] or [G, K] with the K of x")
+    if G > 1 and ldm2 != ldm:
+        raise ValueError("shift and scale must have the same row stride")
+    if rows_per_group is None:
+        if M % G:
+            raise ValueError("pass rows_per_group when G does not divide M")
+        rows_per_group = max(M // G, 1)
+    if M and -(-M // rows_per_group) > G:
+        raise ValueError(f"{-(-M // rows_per_group)} row groups need that many shift/scale rows")
+    xq, s, y = _producer_out(x, M, K, return_y)
+    _check("w8a8_layernorm_modulate_quant_act",
+           lib().w8a8_layernorm_modulate_quant_act(
+               _ptr(x), M, K, ldx, _ptr(shift), _ptr(scale), ldm if G > 1 else K,
+               int(rows_per_group), float(eps), _ptr(xq), _ptr(s), _ptr(y), K,
+               _stream(x.device)))
+    return (xq, s, y) if return_y else (xq, s)
+
+
+def gelu_quant_act(z, approximate: str = "none", return_y: bool = False):
+    """GELU of bf16 z [M, K] ('none': z Phi(z); 'tanh': the tanh form) fused
+    with its per-row int8 quantisation -> (xq, a_scale[, y bf16])."""
+    codes = {"none": GELU_ERF, "tanh": GELU_TANH}
+    if approximate not in codes:
+        raise ValueError("approximate must be 'none' or 'tanh'")
+    M, K, ldz = _rows(z, torch.bfloat16, "z")
+    xq, s, y = _producer_out(z, M, K, return_y)
+    _check("w8a8_gelu_quant_act",
+           lib().w8a8_gelu_quant_act(_ptr(z), M, K, ldz, codes[approximate], _ptr(xq), _ptr(s),
+                                     _ptr(y), K, _stream(z.device)))
+    return (xq, s, y) if return_y else (xq, s)

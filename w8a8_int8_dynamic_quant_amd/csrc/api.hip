@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/w8a8.h"
+#include "producers.h"
 #include "w8a8_kernels.h"
 
 namespace {
@@ -107,6 +108,30 @@ int w8a16_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int
   if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
   w8a8::GemmArgs g{nullptr, nullptr, wq, w_scale, bias, out, nullptr, M, N, K, ldo, f16};
   return hip_status(w8a8::launch_w8a16(x, ldx, g, (hipStream_t)stream));
+}
+
+int producer_common(const w8a8::ProducerArgs& p, void* stream) {
+  if (p.M < 0) return W8A8_ERR_INVALID_ARG;
+  if (int s = check_k(p.K)) return s;
+  if (p.K > w8a8::kProducerMaxK[p.op]) return W8A8_ERR_UNSUPPORTED;
+  if (int s = check_bf16_ld(p.ldx, p.K)) return s;
+  if (p.y) {
+    if (int s = check_bf16_ld(p.ldy, p.K)) return s;
+  }
+  const bool ln = p.op == w8a8::kProducerLayerNorm;
+  if (ln) {
+    if (p.rows_per_group < 1 || !(p.eps > 0.0f) || !(p.eps <= 3.4028235e38f))
+      return W8A8_ERR_INVALID_ARG;
+    if (int s = check_bf16_ld(p.ld_mod, p.K)) return s;
+  }
+  if (p.M == 0) return W8A8_OK;
+  if (!p.x || !p.xq || !p.a_scale) return W8A8_ERR_INVALID_ARG;
+  if (ln && (!p.shift || !p.scale)) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(p.x, 16) || !aligned(p.xq, 16) || !aligned(p.a_scale, 4))
+    return W8A8_ERR_MISALIGNED;
+  if (ln && (!aligned(p.shift, 16) || !aligned(p.scale, 16))) return W8A8_ERR_MISALIGNED;
+  if (p.y && !aligned(p.y, 16)) return W8A8_ERR_MISALIGNED;
+  return hip_status(w8a8::launch_producer_quant(p, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -224,6 +249,24 @@ const char* w8a8_status_string(int status) {
     case W8A8_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }
+}
+
+int w8a8_layernorm_modulate_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                      const uint16_t* shift, const uint16_t* scale,
+                                      int64_t ld_mod, int64_t rows_per_group, float eps,
+                                      int8_t* xq, float* a_scale, uint16_t* y, int64_t ldy,
+                                      void* stream) {
+  w8a8::ProducerArgs p{w8a8::kProducerLayerNorm, x, M, K, ldx, shift, scale, ld_mod,
+                       rows_per_group, eps, xq, a_scale, y, ldy};
+  return producer_common(p, stream);
+}
+
+int w8a8_gelu_quant_act(const uint16_t* z, int64_t M, int64_t K, int64_t ldz, int approximate,
+                        int8_t* xq, float* a_scale, uint16_t* y, int64_t ldy, void* stream) {
+  if (approximate != W8A8_GELU_ERF && approximate != W8A8_GELU_TANH) return W8A8_ERR_INVALID_ARG;
+  const int op = approximate == W8A8_GELU_ERF ? w8a8::kProducerGelu : w8a8::kProducerGeluTanh;
+  w8a8::ProducerArgs p{op, z, M, K, ldz, nullptr, nullptr, 0, 1, 0.0f, xq, a_scale, y, ldy};
+  return producer_common(p, stream);
 }
 
 int w8a8_last_hip_error(void) { return g_last_hip_error; }
