@@ -139,7 +139,8 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
     (bf16 activations, int8 weights) against the W8A8 small-M kernel, both
     HBM-bound (the weight is read once), reported as algorithmic GB/s =
     (2MK + NK + 4N + 2N + 2MN) / t. Pack-quantized ingest of the same weight
-    (N*K/4 words in, N*K int8 + N fp32 out). Each figure is the median over 5
+    (N*K/4 words in, N*K int8 + N fp32 out). The modulated LayerNorm and GELU
+    fused with the quantisation (fused_producers). Each figure is the median over 5
     batches of 60 back-to-back calls bracketed by HIP events, rotating over
     copies of the weight that together exceed the 256 MB last-level cache.
     """
@@ -240,7 +241,73 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
     alg = 2 * N * K + 8 * N
     res["unpack_pack_quantized"] = {"us": us, "gbs": alg / (us * 1e-6) / 1e9,
                                     "pct_hbm": 100 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    del packs, outs
+    res["fused_producers"] = fused_producers(w8, torch, np, dev, timed, ok)
     return res
+
+
+def fused_producers(w8, torch, np, dev, timed, ok) -> dict:
+    """The modulated LayerNorm on the DiT block's 4352 x 3072 input and GELU on
+    its 4352 x 12288 FFN-down input, each fused with the int8 quantisation:
+    algorithmic bytes 2MK (bf16 in) + MK (int8 out) + 4M (scales), plus 4K
+    (shift, scale) for the LayerNorm; the optional bf16 y adds 2MK. Against
+    the two-pass route it replaces: the quantisation kernel alone on a bf16
+    row (what fusion saves, beside the producer's own bf16 write), and
+    torch's bf16 producer ops followed by that quantisation (context only).
+    Inputs and outputs rotate over copies totalling more than 512 MB."""
+    lib = w8.lib()
+    sp = torch.cuda.current_stream(dev)
+    out = {}
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for name, M, K in (("layernorm_modulate", 4352, 3072), ("gelu_tanh", 4352, 12288),
+                       ("gelu_erf", 4352, 12288)):
+        copies = max(2, -(-(512 << 20) // (2 * M * K)))
+        x0 = torch.randn((M, K), generator=g).to(torch.bfloat16)
+        xs = [x0.to(dev) for _ in range(copies)]
+        xqs = [torch.empty((M, K), dtype=torch.int8, device=dev) for _ in range(copies)]
+        sa = torch.empty((M,), dtype=torch.float32, device=dev)
+        y = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        shift = (torch.randn((K,), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        scale = (torch.randn((K,), generator=g) * 0.5).to(torch.bfloat16).to(dev)
+        torch.cuda.synchronize()
+        if name == "layernorm_modulate":
+            def fused(i, yp=None):
+                ok(lib.w8a8_layernorm_modulate_quant_act(
+                    xs[i % copies].data_ptr(), M, K, K, shift.data_ptr(), scale.data_ptr(), K, M,
+                    1e-6, xqs[i % copies].data_ptr(), sa.data_ptr(), yp, K, sp.cuda_stream))
+
+            def producer_torch(xx):
+                h = torch.nn.functional.layer_norm(xx, (K,), eps=1e-6)
+                return h * (1 + scale) + shift
+            mod_bytes = 4 * K
+        else:
+            code = w8.GELU_TANH if name == "gelu_tanh" else w8.GELU_ERF
+            approx = "tanh" if name == "gelu_tanh" else "none"
+
+            def fused(i, yp=None):
+                ok(lib.w8a8_gelu_quant_act(xs[i % copies].data_ptr(), M, K, K, code,
+                                           xqs[i % copies].data_ptr(), sa.data_ptr(), yp, K,
+                                           sp.cuda_stream))
+
+            def producer_torch(xx):
+                return torch.nn.functional.gelu(xx, approximate=approx)
+            mod_bytes = 0
+        alg = 3 * M * K + 4 * M + mod_bytes
+        calls = 60 if K <= 4096 else 20
+        us = timed(lambda i: fused(i), calls=calls)
+        us_y = timed(lambda i: fused(i, y.data_ptr()), calls=calls)
+        us_q = timed(lambda i: ok(lib.w8a8_quant_act(
+            xs[i % copies].data_ptr(), M, K, K, xqs[i % copies].data_ptr(), sa.data_ptr(),
+            sp.cuda_stream)), calls=calls)
+        us_t = timed(lambda i: w8.quant_act(producer_torch(xs[i % copies])), calls=calls)
+        out[name] = {
+            "shape": f"{M}x{K}", "fused_us": us, "fused_gbs": alg / (us * 1e-6) / 1e9,
+            "fused_pct_hbm": 100 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "fused_with_y_us": us_y, "quant_alone_us": us_q,
+            "torch_producer_then_quant_us": us_t}
+        del xs, xqs, y
+        torch.cuda.synchronize()
+    return out
 
 
 def main():

@@ -232,6 +232,50 @@ def test_gelu_full_dit_rows(approximate):
     assert st["n_not_nearest"] <= st["n"] // 1000, st
 
 
+# GELU calls of at least 2^22 elements with K <= 16384 take the table path
+# (the whole bf16 -> bf16 map in LDS); it must give the same bits as the
+# per-element kernel, which smaller calls take.
+LUT_MIN = 1 << 22
+
+
+@pytest.mark.parametrize("approximate", ["none", "tanh"])
+def test_gelu_table_path_every_bf16_value(approximate):
+    z = all_finite_bf16().reshape(16, 4080)
+    big = np.tile(z, (65, 1))                      # 1040 x 4080 rows: the table path
+    assert big.size >= LUT_MIN
+    st = run_gelu(big, approximate)
+    assert st["n_not_nearest"] <= st["n"] // 1000, st
+    # the same rows through the per-element kernel give the same bits
+    zd = dev_bf16(z)
+    announce(f"gelu {approximate} table vs per-element")
+    xq_s, sa_s, y_s = w8.gelu_quant_act(zd, approximate, return_y=True)
+    xq_b, sa_b, y_b = w8.gelu_quant_act(dev_bf16(big), approximate, return_y=True)
+    torch.cuda.synchronize()
+    for r in (0, 16 * 7 + 3, 16 * 64 + 15):
+        assert np.array_equal(host_bits(y_b)[r], host_bits(y_s)[r % 16])
+        assert np.array_equal(host(xq_b)[r], host(xq_s)[r % 16])
+        assert host(sa_b)[r] == host(sa_s)[r % 16]
+
+
+@pytest.mark.parametrize("approximate", ["none", "tanh"])
+@pytest.mark.parametrize("M,K", [(1100, 4112), (262160, 16), (400, 12288), (3001, 1552),
+                                 (520, 8192), (300, 16384)])
+def test_gelu_table_path_shapes(approximate, M, K):
+    """Ragged K (past-K chunks in a lane's last slots), one to eight chunks
+    per lane up to the longest table-path rows (K = 16384), and more rows
+    than the grid takes in one pass."""
+    assert M * K >= LUT_MIN
+    rng = np.random.default_rng(M + K)
+    st = run_gelu(random_bf16(rng, (M, K), 1.5), approximate)
+    assert st["n_not_nearest"] <= max(2, st["n"] // 1000), st
+
+
+@pytest.mark.parametrize("approximate", ["none", "tanh"])
+def test_gelu_table_path_strided(approximate):
+    rng = np.random.default_rng(5)
+    run_gelu(random_bf16(rng, (2100, 2048), 1.0), approximate, ldz=2056)
+
+
 # --- with the GEMM ----------------------------------------------------------
 
 @pytest.mark.parametrize("producer", ["layernorm", "gelu"])

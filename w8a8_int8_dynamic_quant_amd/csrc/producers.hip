@@ -27,11 +27,32 @@
 //   sums are added in part order: no term passes through more than
 //   K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K,
 //   rstd = 1 / sqrt(var + eps), y = ((x - mean) * rstd) * (1 + scale) + shift.
-//   GELU: (0.5 z) * erfc(-z / sqrt 2), which has no cancellation for z << 0.
+//   GELU: (0.5 z) * erfc(-z / sqrt 2), which has no cancellation for z << 0,
+//   with erfc(x) = t exp(-x^2 + P(t)), t = 1 / (1 + x/2), for x = |z| / sqrt 2
+//   (2 - erfc(x) for z > 0): the form of Numerical Recipes' Chebyshev erfc
+//   (section 6.2), P a degree-9 polynomial of our own fit, within 2 fp32 ulps
+//   (gen_erfc_poly.py).
 //   tanh form: with t = sqrt(2/pi) (z + 0.044715 z^3) and e = exp(-2|t|),
 //   z / (1 + e) for t >= 0 and z e / (1 + e) for t < 0 (the same function as
 //   0.5 z (1 + tanh t), without the overflow of exp(-2t) at t << 0).
+//   exp and 1/x are the hardware's v_exp_f32 (2^x) and v_rcp_f32 (each within
+//   about an ulp); an exponent below -64 is raised by 64 and the result scaled
+//   back by 2^-64 at the end, so that results in the subnormal range are kept.
+//   The bf16 rounding is v_cvt_pk_bf16_f32 (nearest even, subnormals kept).
+//
+// GELU on large inputs goes through a table instead: a bf16 input has 65536
+// values, so the whole map z -> bf16(GELU(z)) is 128 KB, which fits in one
+// compute unit's 160 KB of LDS. A small kernel evaluates the map with the
+// fp32 code above (the same bits the per-element kernel produces) into a
+// static device array on the caller's stream; the quantisation kernel then
+// copies it into LDS once per workgroup (one 1024-thread workgroup per
+// compute unit, one or four rows at a time) and replaces the ~30 VALU
+// instructions per element of the formula by one LDS lookup, leaving the row
+// stream HBM-bound. Every call rebuilds the table with the same values, so
+// calls on different streams only ever write identical bytes.
+#include "erfc_poly.h"
 #include "producers.h"
+#include "row_groups.h"
 #include "w8a8_device.h"
 
 namespace w8a8 {
@@ -65,26 +86,50 @@ __device__ __forceinline__ void unpack8(uint4 v, float (&f)[8]) {
   }
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Eight fp32 -> eight bf16 (round to nearest even), packed low to high.
 __device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i)
+    w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){f[2 * i], f[2 * i + 1]}, v2bf));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+constexpr float kLog2e = 1.44269504088896341f;
+
+// GELU in fp32 without branches. 2^q comes from v_exp_f32; where q < -64 it
+// is taken as 2^(q + 64) and the result scaled back by 2^-64 at the end, so
+// results in the fp32 subnormal range are kept. On the positive side such a
+// term is below 2^-64 and drops out of 1 + e (or 2 - erfc) exactly.
 __device__ __forceinline__ float gelu_erf(float z) {
 #pragma clang fp contract(off)
-  const float a = z * -0.707106781186547524f;     // -z / sqrt 2
-  return (0.5f * z) * erfcf(a);
+  const float x = __builtin_fabsf(z) * 0.707106781186547524f;     // |z| / sqrt 2
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(x, 0.5f, 1.0f));
+  float p = kErfcPoly[kErfcPolyDegree];
+#pragma unroll
+  for (int i = kErfcPolyDegree - 1; i >= 0; --i) p = __builtin_fmaf(p, t, kErfcPoly[i]);
+  const float q = (p - x * x) * kLog2e;
+  const bool shifted = q < -64.0f;
+  const float c = t * __builtin_amdgcn_exp2f(shifted ? q + 64.0f : q);   // erfc(x) (* 2^64)
+  const bool pos = z > 0.0f;
+  const float y = (0.5f * z) * (pos ? 2.0f - (shifted ? 0.0f : c) : c);  // erfc(-x) = 2 - erfc(x)
+  return (shifted && !pos) ? y * 0x1p-64f : y;
 }
 
 __device__ __forceinline__ float gelu_tanh(float z) {
 #pragma clang fp contract(off)
   const float z3 = (z * z) * z;
   const float t = 0.797884560802865355f * (z + 0.044715f * z3);   // sqrt(2/pi)
-  const float e = expf(-2.0f * __builtin_fabsf(t));
-  const float den = 1.0f + e;
-  return t >= 0.0f ? z / den : (z * e) / den;
+  const float q = (-2.0f * kLog2e) * __builtin_fabsf(t);
+  const bool shifted = q < -64.0f;
+  const float e = __builtin_amdgcn_exp2f(shifted ? q + 64.0f : q);     // exp(-2|t|) (* 2^64)
+  const float r = __builtin_amdgcn_rcpf(1.0f + (shifted ? 0.0f : e));
+  const bool pos = t >= 0.0f;
+  const float y = (pos ? z : z * e) * r;
+  return (shifted && !pos) ? y * 0x1p-64f : y;
 }
 
 // Adds the WPR per-wave values of this wave's row in part order (the same
@@ -153,29 +198,30 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
     }
   }
 
-  // the producer's bf16 row, in place of x
+  // the producer's row y in fp32, then rounded to bf16 in place of x. The
+  // row's amax is taken on the fp32 values: rounding to nearest even is
+  // monotone and odd, so max |bf16(y)| = bf16(max |y|).
+  float amaxf = 0.0f;
   if constexpr (OP == kProducerLayerNorm) {
 #pragma clang fp contract(off)
+    float f[CH][8];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) unpack8(v[c], f[c]);
     // chunks past K read zero and add nothing to the sum
     float s = 0.0f;
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      float f[8];
-      unpack8(v[c], f);
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = s + f[i];
-    }
+      for (int i = 0; i < 8; ++i) s = s + f[c][i];
     s = row_sum_parts<WPR>(wave_sum(s), red_sum, wave, lane);
     const float mean = s / (float)a.K;
     float q = 0.0f;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (lane + 64 * (part + WPR * c) < (int)nchunks) {
-        float f[8];
-        unpack8(v[c], f);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float d = f[i] - mean;
+          const float d = f[c][i] - mean;
           q = q + d * d;
         }
       }
@@ -185,41 +231,39 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (lane + 64 * (part + WPR * c) < (int)nchunks) {
-        float f[8], fs[8], fh[8];
-        unpack8(v[c], f);
+        float fs[8], fh[8];
         unpack8(sc[c], fs);
         unpack8(sh[c], fh);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float t = f[i] - mean;
+          float t = f[c][i] - mean;
           t = t * rstd;
           t = t * (1.0f + fs[i]);
-          f[i] = t + fh[i];
+          f[c][i] = t + fh[i];
+          amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(f[c][i]));
         }
-        v[c] = pack8_bf16(f);
+        v[c] = pack8_bf16(f[c]);
       } else {
         v[c] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
   } else {
+    // chunks past K read zero, and GELU(0) = 0 in both forms
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (lane + 64 * (part + WPR * c) < (int)nchunks) {
-        float f[8];
-        unpack8(v[c], f);
+      float f[8];
+      unpack8(v[c], f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = OP == kProducerGelu ? gelu_erf(f[i]) : gelu_tanh(f[i]);
-        v[c] = pack8_bf16(f);
-      } else {
-        v[c] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < 8; ++i) {
+        f[i] = OP == kProducerGelu ? gelu_erf(f[i]) : gelu_tanh(f[i]);
+        amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(f[i]));
       }
+      v[c] = pack8_bf16(f);
     }
   }
 
   // per-row quantisation of the bf16 row (the activation quantisation's maths)
-  uint32_t amax = 0;
-#pragma unroll
-  for (int c = 0; c < CH; ++c) amax = absmax_bits8(v[c], amax);
+  uint32_t amax = f32_to_bf16_rne(amaxf);
   amax = row_max_parts<WPR>(wave_max_u32(amax), red_max, wave, lane);
   if (!valid) return;
   const float s = row_scale<false>(amax);
@@ -243,6 +287,144 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
   if (lane == 0 && part == 0) a.a_scale[row] = s;
 }
 
+// z -> bf16(GELU(z)) for every bf16 bit pattern z, erf form then tanh form.
+__device__ __attribute__((aligned(16))) uint16_t g_gelu_table[2][65536];
+
+constexpr int kLutWaves = 16;                        // waves per lookup workgroup
+constexpr size_t kLutBytes = 65536 * sizeof(uint16_t);
+
+template <int OP>
+__global__ __launch_bounds__(256) void gelu_table_kernel() {
+  const uint32_t z = blockIdx.x * 256u + threadIdx.x;          // grid 256 x 256
+  const float zf = bf16_to_f32(z);
+  const float y = OP == kProducerGelu ? gelu_erf(zf) : gelu_tanh(zf);
+  g_gelu_table[OP - kProducerGelu][z] =
+      (uint16_t)__builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){y, 0.0f}, v2bf));
+}
+
+// WPR waves per row (wave part p holds chunks lane + 64 (p + WPR c), c < CH),
+// 16 / WPR rows per iteration of the workgroup. Each wave requests its part
+// of the row DEPTH iterations ahead before it works on the current one, so
+// DEPTH + 1 rows per wave stay in flight; the parts of a row exchange their
+// amax through LDS slots, double-buffered by iteration so one barrier per
+// iteration suffices (no wave runs more than one iteration ahead of
+// another). Every wave of a workgroup runs the same number of iterations; a
+// row past M reads zero and stores nothing.
+template <int OP, int CH, int WPR, int DEPTH>
+__global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(ProducerArgs a) {
+  static_assert(WPR == 4 || WPR == 8 || WPR == 16, "waves per row");
+  static_assert(DEPTH == 1 || DEPTH == 2, "rows requested ahead");
+  constexpr int RPI = kLutWaves / WPR;               // rows per iteration
+  extern __shared__ __attribute__((aligned(16))) uint16_t lut[];
+  __shared__ uint32_t part_max[2][kLutWaves];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(g_gelu_table[OP - kProducerGelu]);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    constexpr int kPer = (int)(kLutBytes / 16) / (64 * kLutWaves);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[threadIdx.x + 64 * kLutWaves * i] = src[threadIdx.x + 64 * kLutWaves * i];
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave % WPR;
+  // byte offset of the lane's first chunk in a row; every offset is in the
+  // vector offset, which the descriptor bound checks, so chunks past K load
+  // zero and their stores are dropped
+  const uint32_t off0 = (uint32_t)(lane + 64 * part) * 16u;
+  constexpr uint32_t kStep = 1024u * WPR;            // bytes between a lane's chunks
+  const int64_t stride = (int64_t)gridDim.x * RPI;
+
+  auto load_row = [&](int64_t row, uint4 (&dst)[CH]) {
+    const bool in = row < a.M;
+    const __amdgpu_buffer_rsrc_t rx =
+        make_rsrc(a.x + (in ? row : 0) * a.ldx, in ? (uint32_t)a.K * 2u : 0u);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) dst[c] = load16_nt(rx, off0 + kStep * c);
+  };
+  int64_t row = (int64_t)blockIdx.x * RPI + wave / WPR;
+  uint4 b[DEPTH + 1][CH];                            // b[0]: this iteration's row
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_row(row + d * stride, b[d]);
+  __syncthreads();                                  // the table is in LDS
+  for (int k = 0; (int64_t)blockIdx.x * RPI + k * stride < a.M; ++k, row += stride) {
+    load_row(row + DEPTH * stride, b[DEPTH]);
+    uint4 (&v)[CH] = b[0];
+    const bool in = row < a.M;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + (in ? row : 0) * a.ldy,
+                                                (a.y && in) ? (uint32_t)a.K * 2u : 0u);
+    // the table maps 0 (a chunk past K) to 0
+    uint32_t amax = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = (uint32_t)lut[w[i] & 0xffffu] | ((uint32_t)lut[w[i] >> 16] << 16);
+        // the packed pair exists before the y store's branch (else both
+        // halves of every chunk stay live until the quantisation)
+        asm volatile("" : "+v"(w[i]));
+      }
+      v[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      amax = absmax_bits8(v[c], amax);
+      if (a.y) store16(v[c], ry, off0 + kStep * c);
+    }
+    amax = wave_max_u32(amax);
+    if (lane == 0) part_max[k & 1][wave] = amax;
+    lds_barrier();
+    const int base = wave - part;
+#pragma unroll
+    for (int p = 0; p < WPR; ++p) amax = max(amax, part_max[k & 1][base + p]);
+    if (in) {
+      const float s = row_scale<false>(amax);
+      const bool zero = (amax == 0);
+      const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;   // subnormal scale
+      const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.xq + row * a.K, (uint32_t)a.K);
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        store8(quant8<false>(v[c], s, r, zero, exact_div), rq, (off0 >> 1) + (kStep >> 1) * c);
+      if (lane == 0 && part == 0) a.a_scale[row] = s;
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) b[d][c] = b[d + 1][c];
+  }
+}
+
+template <int OP, int CH, int WPR, int DEPTH>
+hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((gelu_table_kernel<OP>), dim3(256), dim3(256), 0, stream);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  constexpr int RPI = kLutWaves / WPR;
+  const int64_t wgs_needed = (a.M + RPI - 1) / RPI;
+  const int64_t cus = device_cus();
+  const unsigned grid = (unsigned)(wgs_needed < cus ? wgs_needed : cus);
+  hipLaunchKernelGGL((gelu_lut_quant_kernel<OP, CH, WPR, DEPTH>), dim3(grid), dim3(64 * kLutWaves),
+                     kLutBytes, stream, a);
+  return hipGetLastError();
+}
+
+// The table path pays for its table build (65536 evaluations) from about
+// 4 M elements on; 4 or 16 waves hold a row, at most 2 chunks per lane
+// (rows up to K = 16384 take it).
+constexpr int64_t kLutMinElements = int64_t(1) << 22;
+constexpr int64_t kLutMaxChunks = 2048;
+
+template <int OP>
+hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
+  // waves per row, rows requested ahead: at 4352 x 12288, 4 and 1 ran in
+  // 45 us, 8 and 1 in 50 us, 16 and 2 in 57 us (wider rows mean more waves
+  // at each barrier; deeper prefetch, more register moves)
+  constexpr int W = 4, D = 1;
+  const int64_t per_lane = ((a.K >> 3) + 64 * W - 1) / (64 * W);
+  if (per_lane <= 1) return launch_lut<OP, 1, W, D>(a, stream);
+  if (per_lane <= 2) return launch_lut<OP, 2, W, D>(a, stream);
+  if (per_lane <= 4) return launch_lut<OP, 4, W, D>(a, stream);
+  if (per_lane <= 6) return launch_lut<OP, 6, W, D>(a, stream);
+  return launch_lut<OP, 8, W, D>(a, stream);
+}
+
 template <int OP, int CH, int WPR>
 hipError_t launch_cfg(const ProducerArgs& a, hipStream_t stream) {
   constexpr int RPB = 4 / WPR;
@@ -254,6 +436,9 @@ hipError_t launch_cfg(const ProducerArgs& a, hipStream_t stream) {
 template <int OP>
 hipError_t launch_op(const ProducerArgs& a, hipStream_t stream) {
   const int64_t nchunks = a.K >> 3;
+  if constexpr (OP != kProducerLayerNorm) {
+    if (nchunks <= kLutMaxChunks && a.M * a.K >= kLutMinElements) return launch_gelu_lut<OP>(a, stream);
+  }
   if (nchunks <= 64) return launch_cfg<OP, 1, 1>(a, stream);
   if (nchunks <= 128) return launch_cfg<OP, 2, 1>(a, stream);
   if (nchunks <= 256) return launch_cfg<OP, 2, 2>(a, stream);
