@@ -25,8 +25,11 @@
 //   LayerNorm: each lane sums its 8 CH values in order, a 64-lane butterfly
 //   adds the lanes (every lane ends with the same value) and the WPR wave
 //   sums are added in part order: no term passes through more than
-//   K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K,
-//   rstd = 1 / sqrt(var + eps), y = ((x - mean) * rstd) * (1 + scale) + shift.
+//   K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K
+//   (squares accumulated by fused multiply-add), rstd = 1 / sqrt(var + eps),
+//   y = fma(fma(x, rstd, -(mean rstd)), 1 + scale, shift): two roundings
+//   fewer than the literal order, and the rounding of mean rstd is within
+//   the error the mean itself carries (u |mean| rstd).
 //   GELU: (0.5 z) * erfc(-z / sqrt 2), which has no cancellation for z << 0,
 //   with erfc(x) = t exp(-x^2 + P(t)), t = 1 / (1 + x/2), for x = |z| / sqrt 2
 //   (2 - erfc(x) for z > 0): the form of Numerical Recipes' Chebyshev erfc
@@ -222,12 +225,13 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float d = f[c][i] - mean;
-          q = q + d * d;
+          q = __builtin_fmaf(d, d, q);
         }
       }
     }
     q = row_sum_parts<WPR>(wave_sum(q), red_sq, wave, lane);
     const float rstd = 1.0f / __builtin_sqrtf(q / (float)a.K + a.eps);
+    const float nmr = -(mean * rstd);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       if (lane + 64 * (part + WPR * c) < (int)nchunks) {
@@ -236,10 +240,8 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
         unpack8(sh[c], fh);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float t = f[c][i] - mean;
-          t = t * rstd;
-          t = t * (1.0f + fs[i]);
-          f[c][i] = t + fh[i];
+          const float t = __builtin_fmaf(f[c][i], rstd, nmr);          // (x - mean) rstd
+          f[c][i] = __builtin_fmaf(t, 1.0f + fs[i], fh[i]);
           amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(f[c][i]));
         }
         v[c] = pack8_bf16(f[c]);
