@@ -13,7 +13,7 @@
 // written and the quantisation would have read back.
 //
 // Layout and schedule follow the quantisation kernels: one, two or four
-// waves per row (from K = 1024 and K = 4096 on), lane `lane` of wave part p
+// waves per row (two from K > 1024, four from K > 4096), lane `lane` of wave part p
 // holding the row's 16-byte chunks lane + 64 (p + WPR c), c < CH, all
 // requested at once (non-temporal: x is read once) and kept in registers
 // through every step, so the row is read from HBM once and written once as
@@ -49,7 +49,7 @@
 // fp32 code above (the same bits the per-element kernel produces) into a
 // static device array on the caller's stream; the quantisation kernel then
 // copies it into LDS once per workgroup (one 1024-thread workgroup per
-// compute unit, one or four rows at a time) and replaces the ~30 VALU
+// compute unit, four rows at a time, four waves to a row) and replaces the ~30 VALU
 // instructions per element of the formula by one LDS lookup, leaving the row
 // stream HBM-bound. Every call rebuilds the table with the same values, so
 // calls on different streams only ever write identical bytes.
