@@ -13,7 +13,8 @@ over the timed steps); per-shape figures, the roofline of the dominant kernel
 (the GEMM, bound by int8 MFMA throughput) and the CPU oracle's rate on the
 same step ride along. Inside the timed region HIP events bracket only the
 GEMM launches (an event record costs GPU time); the full per-launch
-breakdown comes from a separate pass after it.
+breakdown comes from a separate pass after it, then a 2.5 s clock pass reads
+the graphics clock and socket power the chip sustains on the step (`sclk`).
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
                     [--no-next-rows]
@@ -128,6 +129,66 @@ def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
         "cpu_model": platform.processor() or platform.machine(),
         "numpy": np.__version__,
     }
+
+
+def clock_pass(step, torch, seconds: float = 2.5):
+    """The graphics clock (per XCD, MHz) and socket power (W) the chip
+    sustains on the block step: amdsmi's GPU metrics, read every 50 ms while
+    the step runs back to back for `seconds`. The metrics table refreshes
+    about once a second, so only readings taken after the first second count
+    (and each distinct reading once). Percent of a published peak depends on
+    this clock. Returns None when amdsmi cannot be used."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception:
+        return None
+    readings, stop = [], threading.Event()
+
+    def sample():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            except Exception:
+                return
+            xcd = [v for v in (m.get("current_gfxclks") or [])
+                   if isinstance(v, (int, float)) and 0 < v < 10000]
+            p = m.get("current_socket_power")
+            readings.append((time.perf_counter() - t0, tuple(xcd),
+                             p if isinstance(p, (int, float)) else None))
+            stop.wait(0.05)
+
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:
+        pass
+    seen, clk, power = set(), [], []
+    for t, xcd, p in readings:
+        if t < 1.0 or not xcd or (xcd, p) in seen:
+            continue
+        seen.add((xcd, p))
+        clk.append(sum(xcd) / len(xcd))
+        if p is not None:
+            power.append(p)
+    if not clk:
+        return None
+    return {"mean_mhz": sum(clk) / len(clk), "min_mhz": min(clk), "max_mhz": max(clk),
+            "per_xcd_mhz": list(xcd), "socket_power_w": sum(power) / len(power) if power else None,
+            "readings": len(clk),
+            "source": (f"amdsmi gpu metrics (current gfx clock averaged over XCDs) read while the "
+                       f"block step ran back to back for {seconds} s after the timed region")}
 
 
 def next_rows(w8, torch, np, dev, to_dev) -> dict:
@@ -426,6 +487,9 @@ def main():
         step(all_events=aev[s])
     torch.cuda.synchronize()
 
+    print("[bench] clock pass", file=sys.stderr, flush=True)
+    sclk = clock_pass(step, torch)
+
     ops_step = sum(2 * L["M"] * L["N"] * L["K"] for L in layers)
     per_shape = []
     gemm_ops = gemm_ms = 0.0
@@ -470,6 +534,11 @@ def main():
         "avg_launch_us": gemm_ms * 1e3 / gemm_launches,
         "ops_per_launch_avg": gemm_ops / gemm_launches,
     }
+    if sclk is not None:
+        # the published peak is quoted at 2.4 GHz; the same MFMA rate at the
+        # clock the chip sustained on this step
+        sclk["int8_peak_at_mean_mhz_tops"] = PEAK_INT8_TOPS * sclk["mean_mhz"] / 2400.0
+        sclk["gemm_frac_at_mean_mhz"] = achieved / sclk["int8_peak_at_mean_mhz_tops"]
 
     line = {
         "metric": METRIC,
@@ -488,13 +557,14 @@ def main():
                    "linears": [f"{L['M']}x{L['K']}x{L['N']}" for L in layers],
                    "tokens": 4352, "hidden": 3072, "mlp": 12288},
         "roofline": roofline,
+        "sclk": sclk,
         "per_shape": per_shape,
         "per_shape_note": ("us/tops/gbs/quant_us: HIP events around every launch in a separate "
                            f"{n_bd}-step pass after the timed region; gemm_us/gemm_tops and "
                            "roofline: events around the GEMM launches inside the timed region"),
     }
     if not args.no_next_rows:
-        print("[bench] next rows (W8A16, ingest, fp16)", file=sys.stderr, flush=True)
+        print("[bench] next rows (W8A16, ingest, fp16, fused producers)", file=sys.stderr, flush=True)
         line["next_rows"] = next_rows(w8, torch, np, dev, to_dev)
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
