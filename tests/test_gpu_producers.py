@@ -276,6 +276,29 @@ def test_gelu_table_path_strided(approximate):
     run_gelu(random_bf16(rng, (2100, 2048), 1.0), approximate, ldz=2056)
 
 
+def test_gelu_table_path_two_streams():
+    """Table-path calls of the same form on two streams at once rebuild the
+    shared table with the same bytes: each result matches its one-stream run."""
+    rng = np.random.default_rng(17)
+    z1, z2 = random_bf16(rng, (1100, 4096), 1.0), random_bf16(rng, (1100, 4096), 2.0)
+    d1, d2 = dev_bf16(z1), dev_bf16(z2)
+    announce("gelu table path, two streams")
+    ref = [w8.gelu_quant_act(d, "none", return_y=True) for d in (d1, d2)]
+    torch.cuda.synchronize()
+    ref = [tuple(host_bits(t) if t.dtype == torch.bfloat16 else host(t) for t in r) for r in ref]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            a = w8.gelu_quant_act(d1, "none", return_y=True)
+        with torch.cuda.stream(s2):
+            b = w8.gelu_quant_act(d2, "none", return_y=True)
+        torch.cuda.synchronize()
+        for got, exp in ((a, ref[0]), (b, ref[1])):
+            assert np.array_equal(host(got[0]), exp[0])
+            assert np.array_equal(host(got[1]), exp[1])
+            assert np.array_equal(host_bits(got[2]), exp[2])
+
+
 # --- with the GEMM ----------------------------------------------------------
 
 @pytest.mark.parametrize("producer", ["layernorm", "gelu"])
