@@ -201,7 +201,8 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
     HBM-bound (the weight is read once), reported as algorithmic GB/s =
     (2MK + NK + 4N + 2N + 2MN) / t. Pack-quantized ingest of the same weight
     (N*K/4 words in, N*K int8 + N fp32 out). The modulated LayerNorm and GELU
-    fused with the quantisation (fused_producers). Each figure is the median over 5
+    fused with the quantisation (fused_producers). The whole linear on the
+    workload table's other configurations (baseline_configs). Each figure is the median over 5
     batches of 60 back-to-back calls bracketed by HIP events, rotating over
     copies of the weight that together exceed the 256 MB last-level cache.
     """
@@ -304,7 +305,48 @@ def next_rows(w8, torch, np, dev, to_dev) -> dict:
                                     "pct_hbm": 100 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     del packs, outs
     res["fused_producers"] = fused_producers(w8, torch, np, dev, timed, ok)
+    res["baseline_configs"] = baseline_configs(w8, torch, dev, to_dev, timed, ok)
     return res
+
+
+def baseline_configs(w8, torch, dev, to_dev, timed, ok) -> dict:
+    """The whole linear (w8a8_linear) on the other configurations of the
+    workload table: the probe shapes (64x256x128 with bias, 512x4096x4096
+    with outlier channels, 512x4096x12288 Student-t with bias) and the
+    modulation projection at M = 2, 17, 32 (M = 17 and 32 take the GEMM
+    path). Weights rotate over copies totalling more than 512 MB; algorithmic
+    bytes 2MK + NK + 4N (+ 2N bias) + 2MN."""
+    from synth_inputs import make_linear_inputs
+    lib = w8.lib()
+    sp = torch.cuda.current_stream(dev)
+    out = {}
+    for name in ("c1_64x256x128", "c2_512x4096x4096_outliers", "c3_512x4096x12288_student_t",
+                 "mod_m2_3072x18432", "mod_m17_3072x18432", "mod_m32_3072x18432"):
+        d = make_linear_inputs(name)
+        M, K, N = d["M"], d["K"], d["N"]
+        wq0, sw = w8.quantize_weights(to_dev(d["w"]))
+        copies = max(1, min(40, -(-(512 << 20) // (N * K))))
+        wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+        x = to_dev(d["x"])
+        bias = None if d["bias"] is None else to_dev(d["bias"])
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((max(w8.workspace_bytes(M, K, N), 1),), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        us = timed(lambda i: ok(lib.w8a8_linear(
+            x.data_ptr(), M, K, K, wqs[i % copies].data_ptr(), sw.data_ptr(), N,
+            None if bias is None else bias.data_ptr(), y.data_ptr(), N, ws.data_ptr(),
+            ws.numel(), None, sp.cuda_stream)))
+        alg = 2 * M * K + N * K + 4 * N + (2 * N if bias is not None else 0) + 2 * M * N
+        ops = 2 * M * N * K
+        out[name] = {"us": us, "tops": ops / (us * 1e-6) / 1e12,
+                     "pct_int8_peak": 100 * ops / (us * 1e-6) / 1e12 / PEAK_INT8_TOPS,
+                     "gbs": alg / (us * 1e-6) / 1e9,
+                     "pct_hbm": 100 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "path": "small_m" if w8.linear_path(M, K, N) == w8.PATH_SMALL_M else "gemm",
+                     "weight_copies": copies}
+        del wqs, x, y, ws
+        torch.cuda.synchronize()
+    return out
 
 
 def fused_producers(w8, torch, np, dev, timed, ok) -> dict:

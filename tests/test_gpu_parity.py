@@ -298,13 +298,13 @@ def test_linear_small_m_work_splits(M, N, K):
     print(_linear_case(x, w, b)[0])
 
 
-@pytest.mark.parametrize("N", [512, 516, 514])
+@pytest.mark.parametrize("N", [2056, 2052, 2050])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_linear_256_tile_store_paths(N, with_bias):
     """The 256x256 tile with each output store path: 16-byte rows staged in
     LDS (N % 8 == 0), 8-byte stores (N % 4 == 0) and 2-byte stores, with and
     without bias."""
-    M, K = 520, 272
+    M, K = 4352, 272
     assert w8.gemm_tile(M, K, N) == (256, 256)
     rng = np.random.default_rng(N * 3 + with_bias)
     x = random_bf16(rng, (M, K))
