@@ -121,11 +121,20 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     bytes, 16-byte aligned, owned by the caller. After the call it holds the
  *     quantised activations xq [M, K] int8 (row stride K) at byte offset 0 and
  *     a_scale [M] fp32 at byte offset W8A8_ALIGN256(M*K), on both paths.
+ *     For shapes that keep 256x256 tiles but fill under half of the compute
+ *     units with them (N % 8 == 0, K above 896; w8a8_gemm_tile reports the
+ *     tile), the size also covers two slices of int32 partial sums after
+ *     a_scale: the GEMM then splits K in two and a second kernel adds the
+ *     partial sums before the epilogue (exact in int32, so the results are
+ *     the same bits). The size depends on the current device's compute-unit
+ *     count.
  *   acc_debug [M, N] int32 or NULL, as in w8a8_scaled_mm.
  * Path: M <= W8A8_SMALL_M (and K <= 8192) runs one fused weight-streaming
  * kernel that quantises x on chip; otherwise the activation quantisation
- * kernel runs first and the MFMA GEMM second. Both paths give bit-identical
- * xq, a_scale, acc and out for the same row.
+ * kernel runs first and the MFMA GEMM second (split as above where the
+ * workspace holds the partial sums and the output rows are 16-byte aligned
+ * with ldo % 8 == 0). All paths give bit-identical xq, a_scale, acc and out
+ * for the same row.
  */
 int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                 const int8_t* wq, const float* w_scale, int64_t N,

@@ -140,6 +140,16 @@ def test_workspace_and_path_queries():
     assert w8.linear_path(-1, 64, 8) == w8.ERR_INVALID_ARG
     bm, bn = w8.gemm_tile(4352, 3072, 9216)
     assert bm >= 128 and bn >= 128
+    # split K (on a device of 256 compute units, the count assumed without a
+    # GPU): the workspace adds int32 partial sums after xq and a_scale
+    base = lambda M, K: ((M * K + 255) // 256) * 256 + ((4 * M + 255) // 256) * 256
+    assert w8.workspace_bytes(512, 4096, 12288) == base(512, 4096) + 2 * 512 * 12288 * 4
+    assert w8.workspace_bytes(700, 2000, 8200) == base(700, 2000) + 2 * 700 * 8200 * 4
+    assert w8.workspace_bytes(512, 4096, 4096) == base(512, 4096)        # 128x128 tiles
+    assert w8.workspace_bytes(4352, 3072, 9216) == base(4352, 3072)      # enough tiles
+    assert w8.workspace_bytes(512, 4096, 12296) == base(512, 4096) + 2 * 512 * 12296 * 4
+    assert w8.workspace_bytes(512, 4096, 12292) == base(512, 4096)       # N % 8 != 0
+    assert w8.workspace_bytes(512, 768, 12288) == base(512, 768)         # K too short
 
 
 def test_unpack_validation():

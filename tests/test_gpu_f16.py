@@ -188,3 +188,15 @@ def test_f16_256_tile_with_bias(N):
     b = random_f16(rng, (N,), 0.01)
     announce(f"f16 256 tile M={M} N={N} K={K} bias")
     print(_linear_case(x, w, b)[0])
+
+
+def test_f16_linear_split_k():
+    """fp16 output and bias through the split-K reduction (see the bf16 test)."""
+    M, N, K = 700, 8200, 2000
+    assert w8.workspace_bytes(M, K, N) > M * K + 4 * M + 512
+    rng = np.random.default_rng(41)
+    x = random_f16(rng, (M, K))
+    w = random_f16(rng, (N, K), 0.02)
+    b = random_f16(rng, (N,), 0.01)
+    announce(f"fp16 split-K linear M={M} N={N} K={K}")
+    _linear_case(x, w, b)

@@ -312,3 +312,35 @@ def test_linear_256_tile_store_paths(N, with_bias):
     b = random_bf16(rng, (N,), 0.01) if with_bias else None
     announce(f"256 tile store path M={M} N={N} K={K} bias={with_bias}")
     print(_linear_case(x, w, b)[0])
+
+
+# Split K: shapes that keep 256x256 tiles but fill under half of the compute
+# units; w8a8_linear then splits K in two (its workspace holds the partial
+# sums), w8a8_scaled_mm does not. Both must give the oracle's acc and the same
+# y bits. (520 x 1040: nine K stages, the second split ends on a 16-byte tail.)
+@pytest.mark.parametrize("M,N,K,with_bias", [(512, 12288, 4096, True), (700, 8200, 2000, True),
+                                             (520, 10240, 1040, False)])
+def test_linear_split_k(M, N, K, with_bias):
+    assert w8.workspace_bytes(M, K, N) > M * K + 4 * M + 512, "the split path is taken"
+    rng = np.random.default_rng(M + N + K)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    b = random_bf16(rng, (N,), 0.01) if with_bias else None
+    announce(f"split-K linear M={M} N={N} K={K} bias={with_bias}")
+    _, exp = _linear_case(x, w, b)
+    wq, sw = w8.quantize_weights(dev_bf16(w))
+    bd = None if b is None else dev_bf16(b)
+    y_split = w8.linear(dev_bf16(x), wq, sw, bd)
+    y_one = w8.scaled_mm(dev(exp["xq"]), dev(exp["s_a"]), wq, sw, bd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y_split), host_bits(y_one))
+
+
+def test_linear_split_k_fallback_on_unaligned_output():
+    """An output row stride that is not a multiple of 8 takes the one-pass GEMM."""
+    M, N, K = 512, 12288, 2048
+    rng = np.random.default_rng(5)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    announce("split-K shape, output stride N + 4")
+    _linear_case(x, w, None, ldo=N + 4)

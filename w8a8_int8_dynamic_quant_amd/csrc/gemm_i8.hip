@@ -148,9 +148,11 @@ __device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
   }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS, bool F16>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S, bool HAS_BIAS, bool F16,
+          bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArgs a, int tiles_m,
-                                                                         int tiles_n, int vec_flags) {
+                                                                         int tiles_n, int vec_flags,
+                                                                         int kps) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int FM = WM / 32, FN = WN / 32;
@@ -188,6 +190,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   const uint32_t rows_x = (uint32_t)min<int64_t>(BM, M - m0);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq + n0 * K, rows_w * (uint32_t)K);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq + m0 * K, rows_x * (uint32_t)K);
+  // bytes of K this workgroup reads (chunks at or past it go out of bounds)
+  const int kend = (int)min<int64_t>(K, (int64_t)min<int64_t>((int64_t)(blockIdx.y + 1) * kps,
+                                                              (K + BK - 1) / BK) * BK);
 
   // Scales and bias of the tile into LDS (zero past M / N); the first stage
   // barrier of the K loop makes them visible to every wave.
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   }
   auto issue = [&](int kt, int8_t* st) {
     const int k0 = kt * BK;
-    const int klim = (int)K - k0;
+    const int klim = kend - k0;
 #pragma unroll
     for (int j = 0; j < LW; ++j) {
       // chunks past K (only in a K-tail stage) go out of bounds, branch-free
@@ -256,7 +261,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
     fw_base[ks] = (wave_n * WN + frag_row) * BK + 16 * swz<BK>(frag_row, 2 * ks + frag_half);
     fx_base[ks] = BN * BK + (wave_m * WM + frag_row) * BK + 16 * swz<BK>(frag_row, 2 * ks + frag_half);
   }
-  const int nk = (int)((K + BK - 1) / BK);
+  // K stages of this workgroup: all of them, or with split K (grid.y > 1)
+  // stages kb .. ke-1; loads past ke*BK go out of bounds (read nothing)
+  const int nk_all = (int)((K + BK - 1) / BK);
+  const int kb = (int)blockIdx.y * kps;
+  const int ke = min(nk_all, kb + kps);
 
   // One stage: read the fragments of k-step 0, then run the MFMAs of each
   // k-step with the next k-step's fragment reads spread between them. With
@@ -291,9 +300,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   // everyone done reading the buffer about to be refilled). The last stage's
   // "next" loads have K offsets past the end, so they only write zeros into
   // the idle buffer, which keeps every stage body identical.
-  issue(0, lds0);
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
+  issue(kb, lds0);
+  int kt = kb;
+  for (; kt + 1 < ke; kt += 2) {
     wait_vmcnt_lgkm0<0>();
     stage_barrier();
     stage(kt, lds0, lds1, std::true_type{});
@@ -301,10 +310,35 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
     stage_barrier();
     stage(kt + 1, lds1, lds0, std::true_type{});
   }
-  if (kt < nk) {
+  if (kt < ke) {
     wait_vmcnt_lgkm0<0>();
     stage_barrier();
     stage(kt, lds0, lds1, std::true_type{});
+  }
+
+  // Split K: this workgroup's int32 partial sums, 16-byte stores of four
+  // consecutive columns (N % 8 == 0 on this path) into slice blockIdx.y; the
+  // reduction kernel adds the slices and applies the epilogue.
+  if constexpr (SPLIT) {
+    const __amdgpu_buffer_rsrc_t r_p =
+        make_rsrc(a.partial + ((int64_t)blockIdx.y * M + m0) * N + n0,
+                  (uint32_t)(((int64_t)(rows_x - 1) * N + rows_w) * 4));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = wave_m * WM + 32 * j + frag_row;
+        const v16i& c = acc[i][j];
+        // four-column runs q = 0..3 are elements 4q..4q+3: register sub-ranges
+        const v4i run[4] = {c.lo.lo, c.lo.hi, c.hi.lo, c.hi.hi};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = wave_n * WN + 32 * i + 8 * q + 4 * frag_half;
+          const uint32_t off = (nl < (int)rows_w) ? (uint32_t)(ml * N + nl) * 4u : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(run[q], r_p, off, 0, 0);
+        }
+      }
+    return;
   }
 
   // Epilogue. Lane holds, for output row m = mb + lane%32, the columns
@@ -416,15 +450,61 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   }
 }
 
+// Split K, second step: out[m, n..n+7] = epilogue(sum over the slices of
+// the int32 partial sums), in the GEMM epilogue's fp32 order; one thread per
+// eight columns (N % 8 == 0, out rows 16-byte aligned). The int32 sum is
+// exact whatever the split, so the result is bit-identical to the one-pass
+// GEMM.
+template <bool HAS_BIAS, bool F16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs a, int splits) {
+  const int64_t n8 = a.N >> 3;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= a.M * n8) return;
+  const int64_t m = g / n8, n = (g - m * n8) * 8;
+  const int64_t slice = a.M * a.N;
+  const int32_t* p = a.partial + m * a.N + n;
+  int acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int sidx = 0; sidx < splits; ++sidx) {
+    const int4 lo = *reinterpret_cast<const int4*>(p + sidx * slice);
+    const int4 hi = *reinterpret_cast<const int4*>(p + sidx * slice + 4);
+    acc[0] += lo.x; acc[1] += lo.y; acc[2] += lo.z; acc[3] += lo.w;
+    acc[4] += hi.x; acc[5] += hi.y; acc[6] += hi.z; acc[7] += hi.w;
+  }
+  if (a.acc_debug) {
+    int32_t* d = a.acc_debug + m * a.N + n;
+    *reinterpret_cast<int4*>(d) = make_int4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<int4*>(d + 4) = make_int4(acc[4], acc[5], acc[6], acc[7]);
+  }
+  const float sa = a.a_scale[m];
+  uint32_t y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float b0 = HAS_BIAS ? half_to_f32<F16>(a.bias[n + 2 * i]) : 0.f;
+    const float b1 = HAS_BIAS ? half_to_f32<F16>(a.bias[n + 2 * i + 1]) : 0.f;
+    const float t0 = epilogue_f32<HAS_BIAS>(acc[2 * i], sa, a.w_scale[n + 2 * i], b0);
+    const float t1 = epilogue_f32<HAS_BIAS>(acc[2 * i + 1], sa, a.w_scale[n + 2 * i + 1], b1);
+    y[i] = pack_half2<F16>(t0, t1);
+  }
+  *reinterpret_cast<uint4*>(a.out + m * a.ldo + n) = make_uint4(y[0], y[1], y[2], y[3]);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int S>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int kps = 0) {
   const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   const int vec_flags = epilogue_vec_flags(a);
-  dim3 grid((unsigned)tiles), block(64 * WAVES_M * WAVES_N);
+  if (splits == 1) kps = (int)((a.K + BK - 1) / BK);
+  dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * WAVES_M * WAVES_N);
+  if constexpr (BM == 256 && BN == 256) {
+    if (splits > 1) {         // partial sums only: bias and output type do not matter
+      hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, false, false, true>),
+                         grid, block, 0, stream, a, (int)tiles_m, (int)tiles_n, vec_flags, kps);
+      return hipGetLastError();
+    }
+  }
 #define W8A8_GEMM(B, H)                                                                    \
   hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, B, H>), grid, block, 0, \
-                     stream, a, (int)tiles_m, (int)tiles_n, vec_flags)
+                     stream, a, (int)tiles_m, (int)tiles_n, vec_flags, kps)
   if (a.f16) {
     if (a.bias) W8A8_GEMM(true, true);
     else W8A8_GEMM(false, true);
@@ -434,6 +514,32 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   }
 #undef W8A8_GEMM
   return hipGetLastError();
+}
+
+// Split-K plan for a shape: when the tile choice keeps 256x256 tiles but
+// they fill under half of the compute units (and K has at least 8 stages),
+// K is split in two, so twice the workgroups stream panels. More splits lose:
+// each adds a slice of int32 partial sums, written and read back (measured on
+// 512x4096x12288: 58 -> 52.6 us with two; 512x4096x4096 with 8 and
+// 1024x4096x4096 with 4 were slower than 128x128 tiles unsplit, 43 against
+// 41 and 57 against 49 us). splits = 1: no split.
+struct SplitPlan {
+  int splits = 1;
+  int kps = 0;              // K stages per split
+};
+
+SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+  SplitPlan p;
+  if ((N & 7) != 0 || N > (int64_t(1) << 21)) return p;
+  int bm, bn;
+  gemm_pick_tile(M, N, K, &bm, &bn);
+  if (bm != 256) return p;
+  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t nk = (K + 127) / 128;
+  if (2 * tiles256 >= device_cus() || nk < 8) return p;
+  p.kps = (int)((nk + 1) / 2);
+  p.splits = (int)((nk + p.kps - 1) / p.kps);
+  return p;
 }
 
 }  // namespace
@@ -454,13 +560,43 @@ void gemm_pick_tile(int64_t M, int64_t N, int64_t K, int* bm, int* bn) {
   *bm = 128; *bn = 128;
 }
 
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan p = split_plan(M, N, K);
+  return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
+  if (a.partial) {
+    // split K only where the output takes the reduction's 16-byte stores
+    const int vf = epilogue_vec_flags(a);
+    const SplitPlan p = split_plan(a.M, a.N, a.K);
+    if (p.splits > 1 && (vf & 4) && (!a.acc_debug || (vf & 2))) {
+      if (hipError_t e = launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps);
+          e != hipSuccess)
+        return e;
+      const int64_t groups = a.M * (a.N >> 3);
+      const dim3 grid((unsigned)((groups + 255) / 256)), block(256);
+#define W8A8_RED(B, H) \
+      hipLaunchKernelGGL((splitk_reduce_kernel<B, H>), grid, block, 0, stream, a, p.splits)
+      if (a.f16) {
+        if (a.bias) W8A8_RED(true, true);
+        else W8A8_RED(false, true);
+      } else {
+        if (a.bias) W8A8_RED(true, false);
+        else W8A8_RED(false, false);
+      }
+#undef W8A8_RED
+      return hipGetLastError();
+    }
+  }
+  GemmArgs one = a;
+  one.partial = nullptr;
   int bm, bn;
   gemm_pick_tile(a.M, a.N, a.K, &bm, &bn);
-  if (bm == 256) return launch_cfg<256, 256, 2, 2, 128, 2>(a, stream);
-  if (bm == 128) return launch_cfg<128, 128, 2, 2, 128, 2>(a, stream);
-  return launch_cfg<64, 64, 2, 2, 64, 2>(a, stream);
+  if (bm == 256) return launch_cfg<256, 256, 2, 2, 128, 2>(one, stream);
+  if (bm == 128) return launch_cfg<128, 128, 2, 2, 128, 2>(one, stream);
+  return launch_cfg<64, 64, 2, 2, 64, 2>(one, stream);
 }
 
 }  // namespace w8a8

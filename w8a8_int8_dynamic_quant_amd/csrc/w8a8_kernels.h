@@ -22,6 +22,10 @@ struct GemmArgs {
   int32_t* acc_debug;      // [M, N] or nullptr
   int64_t M, N, K, ldo;
   bool f16 = false;        // bias, out (and the small-M kernel's x) are fp16, not bf16
+  // split-K: int32 partial sums [splits][M][N] (a workspace of at least
+  // gemm_partial_bytes(M, N, K) bytes), or nullptr to compute every tile in
+  // one workgroup
+  int32_t* partial = nullptr;
 };
 
 // Bit 0: out rows allow 8-byte stores of four bf16 (out 8-byte aligned,
@@ -43,8 +47,15 @@ inline int epilogue_vec_flags(const GemmArgs& a) {
 // Tile (BM x BN) the MFMA GEMM picks for a shape.
 void gemm_pick_tile(int64_t M, int64_t N, int64_t K, int* bm, int* bn);
 
-// int8 MFMA GEMM with the fused scale epilogue.
+// int8 MFMA GEMM with the fused scale epilogue. With a.partial set and a
+// shape whose large tiles leave most compute units idle, K is split in two
+// and a second kernel adds the int32 partial sums (exactly) before the same
+// epilogue.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+// Bytes of partial sums launch_gemm uses for this shape on the current
+// device (0: no split).
+size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K);
 
 // Small-M path: per-row activation quantisation on chip + weight-streaming
 // MFMA product + epilogue, one kernel. Also writes xq/a_scale to xq_out /
