@@ -520,7 +520,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
 // they fill under half of the compute units (and K has at least 8 stages),
 // K is split in two, so twice the workgroups stream panels. More splits lose:
 // each adds a slice of int32 partial sums, written and read back (measured on
-// 512x4096x12288: 58 -> 52.6 us with two; 512x4096x4096 with 8 and
+// 512x4096x12288: 58 -> 53-55 us with two; 512x4096x4096 with 8 and
 // 1024x4096x4096 with 4 were slower than 128x128 tiles unsplit, 43 against
 // 41 and 57 against 49 us). splits = 1: no split.
 struct SplitPlan {
