@@ -20,7 +20,8 @@
  * - unsloth test_diffusion_transformer_quant.py commit log: int8 products
  *   accumulate in int32; the torch._int_mm route needs M > 16 and so could
  *   not serve the M = 1 modulation projections. This library has no such
- *   limit: M <= W8A8_SMALL_M goes to a bandwidth-bound small-M kernel.
+ *   limit: M <= W8A8_SMALL_M (M <= W8A8_SMALL_M_WIDE for K <= 4096) goes to
+ *   a bandwidth-bound small-M kernel.
  *
  * Per-row quantisation of a row r[0..K-1]:
  *   amax = max_k |r[k]|,  scale = fl32(amax / 127)   (IEEE fp32 division)
@@ -67,8 +68,10 @@ typedef enum {
 
 /* Largest K whose worst-case accumulator 127*127*K fits in int32. */
 #define W8A8_K_MAX 133144
-/* Rows up to this count take the small-M (weight-streaming) path. */
+/* Rows up to this count take the small-M (weight-streaming) path when
+ * K <= 8192; up to W8A8_SMALL_M_WIDE rows take it when K <= 4096. */
 #define W8A8_SMALL_M 16
+#define W8A8_SMALL_M_WIDE 32
 /* Largest output leading dimension (elements; the debug accumulators allow
  * N up to half of it): kernels address a 256-row output tile with 32-bit
  * byte offsets. Larger values give W8A8_ERR_UNSUPPORTED. */
@@ -129,8 +132,8 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     the same bits). The size depends on the current device's compute-unit
  *     count.
  *   acc_debug [M, N] int32 or NULL, as in w8a8_scaled_mm.
- * Path: M <= W8A8_SMALL_M (and K <= 8192) runs one fused weight-streaming
- * kernel that quantises x on chip; otherwise the activation quantisation
+ * Path: M <= W8A8_SMALL_M with K <= 8192, or M <= W8A8_SMALL_M_WIDE with
+ * K <= 4096, runs one fused weight-streaming kernel that quantises x on chip; otherwise the activation quantisation
  * kernel runs first and the MFMA GEMM second (split as above where the
  * workspace holds the partial sums and the output rows are 16-byte aligned
  * with ldo % 8 == 0). All paths give bit-identical xq, a_scale, acc and out

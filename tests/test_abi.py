@@ -36,6 +36,7 @@ def test_constants_match_header():
     text = open(HEADER).read()
     assert f"#define W8A8_K_MAX {w8.K_MAX}" in text
     assert f"#define W8A8_SMALL_M {w8.SMALL_M}" in text
+    assert f"#define W8A8_SMALL_M_WIDE {w8.SMALL_M_WIDE}" in text
     assert "#define W8A8_LDO_MAX (1 << 22)" in text and w8.LDO_MAX == 1 << 22
     assert w8.K_MAX == (2**31 - 1) // (127 * 127)
 
@@ -129,13 +130,15 @@ def test_workspace_and_path_queries():
     assert w8.workspace_bytes(1, 64, 8) == 256 + 256
     assert w8.workspace_bytes(4352, 3072, 9216) == 4352 * 3072 + 17408
     assert w8.linear_path(0, 64, 8) == w8.PATH_NONE
-    for m in (1, 2, 8, 16):
+    for m in (1, 2, 8, 16, 17, 32):
         assert w8.linear_path(m, 3072, 18432) == w8.PATH_SMALL_M
-    for m in (17, 32, 4352):
+    for m in (33, 4352):
         assert w8.linear_path(m, 3072, 18432) == w8.PATH_GEMM
-    # the small-M kernel keeps K in LDS: longer rows use the GEMM
-    assert w8.linear_path(1, 8192, 64) == w8.PATH_SMALL_M
+    # the small-M kernel keeps the quantised rows in LDS: longer rows use the GEMM
+    assert w8.linear_path(16, 8192, 64) == w8.PATH_SMALL_M
     assert w8.linear_path(1, 8208, 64) == w8.PATH_GEMM
+    assert w8.linear_path(32, 4096, 64) == w8.PATH_SMALL_M
+    assert w8.linear_path(17, 4112, 64) == w8.PATH_GEMM
     assert w8.linear_path(4, 20, 8) == w8.ERR_UNSUPPORTED
     assert w8.linear_path(-1, 64, 8) == w8.ERR_INVALID_ARG
     bm, bn = w8.gemm_tile(4352, 3072, 9216)

@@ -200,15 +200,18 @@ def test_linear_strided_x_and_out():
 
 
 def test_small_m_and_gemm_paths_agree_per_row():
-    """Row m gives the same xq, a_scale, acc and y at M=16 (small-M kernel)
-    and M=17 (quantisation kernel + GEMM)."""
-    d = make_linear_inputs("mod_m17_3072x18432")
+    """Row m gives the same xq, a_scale, acc and y at M = 16 (small-M kernel,
+    two token blocks), M = 32 (small-M kernel, four token blocks) and M = 33
+    (quantisation kernel + GEMM)."""
+    d = make_linear_inputs("mod_m32_3072x18432")
+    extra = random_bf16(np.random.default_rng(33), (1, 3072))
+    x_all = np.concatenate([d["x"], extra])
     wq, sw = w8.quantize_weights(dev_bf16(d["w"]))
     bd = dev_bf16(d["bias"])
     res = {}
-    for M in (16, 17):
-        assert w8.linear_path(M, 3072, 18432) == (w8.PATH_SMALL_M if M == 16 else w8.PATH_GEMM)
-        x = dev_bf16(d["x"][:M])
+    for M in (16, 32, 33):
+        assert w8.linear_path(M, 3072, 18432) == (w8.PATH_SMALL_M if M <= 32 else w8.PATH_GEMM)
+        x = dev_bf16(x_all[:M])
         acc = torch.empty((M, 18432), dtype=torch.int32, device="cuda")
         ws = torch.empty((w8.workspace_bytes(M, 3072, 18432),), dtype=torch.uint8, device="cuda")
         announce(f"path agreement M={M}")
@@ -216,8 +219,9 @@ def test_small_m_and_gemm_paths_agree_per_row():
         torch.cuda.synchronize()
         xq, sa = w8.workspace_views(ws, M, 3072)
         res[M] = [host(xq), host(sa), host(acc), host_bits(y)]
-    for a, b in zip(res[16], res[17]):
-        assert np.array_equal(a[:16], b[:16])
+    for a, b, c in zip(res[16], res[32], res[33]):
+        assert np.array_equal(a, b[:16])
+        assert np.array_equal(b, c[:32])
 
 
 def test_fused_qkv_equals_three_calls():
@@ -282,13 +286,15 @@ def test_linear_subnormal_scales_and_outputs():
 
 
 @pytest.mark.parametrize("M,N,K", [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040),
-                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088)])
+                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088),
+                                   (17, 70, 1040), (25, 200, 3072), (32, 18432, 3072),
+                                   (24, 70, 3088), (32, 33, 4096)])
 def test_linear_small_m_work_splits(M, N, K):
     """Every way the small-M kernel splits the activation rows over its waves
-    (W = 4 waves for N = 70 and 200, 9 for N = 18432): one row per wave
+    (W = 4 waves for N = 33, 70 and 200, 9 for N = 18432): one row per wave
     (M <= W), two rows per wave held across the weight requests (W < M <=
-    2W), rows quantised before the stream (M > 2W) and rows longer than the
-    register-resident limit (K > 3072)."""
+    2W), rows quantised before the stream (M > 2W, and every M above 16) and
+    rows longer than the register-resident limit (K > 3072)."""
     rng = np.random.default_rng(M * 31 + N + K)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)

@@ -33,7 +33,8 @@ ERR_MISALIGNED = -3
 ERR_WORKSPACE = -4
 ERR_HIP = -5
 K_MAX = 133144
-SMALL_M = 16
+SMALL_M = 16          # small-M path for K <= 8192
+SMALL_M_WIDE = 32     # ... and up to this M for K <= 4096
 LDO_MAX = 1 << 22
 PATH_NONE, PATH_SMALL_M, PATH_GEMM = 0, 1, 2
 SCALE_F32, SCALE_BF16, SCALE_F16 = 0, 1, 2

@@ -60,7 +60,9 @@ int check_gemm(int64_t M, int64_t K, int64_t N, const int8_t* wq, const float* w
 }
 
 bool small_m_path(int64_t M, int64_t K) {
-  return M >= 1 && M <= W8A8_SMALL_M && K <= w8a8::kSmallMMaxK;
+  static_assert(W8A8_SMALL_M_WIDE == w8a8::kSmallMWideRows, "small-M row limits");
+  return M >= 1 && ((M <= W8A8_SMALL_M && K <= w8a8::kSmallMMaxK) ||
+                    (M <= W8A8_SMALL_M_WIDE && K <= w8a8::kSmallMWideMaxK));
 }
 
 int scaled_mm_common(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,

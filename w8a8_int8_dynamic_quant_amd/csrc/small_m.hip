@@ -1,4 +1,4 @@
-// Small-M W8A8 linear (M <= 16): one fused, weight-streaming kernel (gfx950).
+// Small-M W8A8 linear (M <= 32): one fused, weight-streaming kernel (gfx950).
 // Activations, bias and output are bf16, or all fp16 (same arithmetic).
 //
 // The int8 matmul route of the prior art requires more than 16 activation
@@ -21,7 +21,8 @@
 //  2. the wave requests up to kD 128-byte windows of its rows at once
 //     (one buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte
 //     chunk l/8, so every instruction fetches 8 whole 128-byte lines).
-//     Each window is one v_mfma_i32_16x16x64_i8 per 8 tokens. The loaded
+//     Each window is one v_mfma_i32_16x16x64_i8 per block of 8 tokens (up
+//     to 4 blocks). The loaded
 //     layout is the MFMA "A" layout if A-row i is read as weight row i%8 at
 //     chunk parity i/8: lane l holds A[l%16][k-group l/16] = row l%8, chunk
 //     2*(l/16) + (l/8)%2 = l/8. The "B" operand is built the same way from
@@ -46,9 +47,10 @@ constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight
 
 // Work split of a launch: ONE_ROW: M <= W and K <= kShortK (a wave quantises
 // at most one activation row, overlapped with the weight stream); TWO_ROWS:
-// the same with up to two rows per wave (M <= 2W, bf16); SHORT: K <=
+// the same with up to two rows per wave (M <= 2W, M <= 16, bf16); SHORT: K <=
 // kShortK, rows quantised before the stream; LONG: longer rows (read twice
-// for quantisation, weight windows refilled as they are consumed).
+// for quantisation, weight windows refilled as they are consumed). Above 16
+// rows (four token blocks) only SHORT and LONG are used.
 enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3 };
 
 // LDS row stride for the quantised activations: K rounded up to whole
@@ -59,21 +61,22 @@ enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3 };
 __host__ __device__ inline int xs_stride(int64_t K) { return (int)((K + 127) / 128) * 128 + 32; }
 
 
-// Quantises the row chunks held in v (chunk lane + 64*u of the row, u < kQ)
+// Quantises the row chunks held in v (chunk lane + 64*u of the row, u < Q)
 // with the row's scale; returns the scale.
-template <bool F16>
-__device__ __forceinline__ float quantise_regs(const uint4 (&v)[kQ], uint32_t nchunks, int lane,
+template <bool F16, int Q = kQ>
+__device__ __forceinline__ float quantise_regs(const uint4 (&v)[Q], uint32_t nchunks, int lane,
                                                int8_t* xrow, int8_t* qrow, bool write_q) {
   uint32_t amax = 0;
 #pragma unroll
-  for (int u = 0; u < kQ; ++u) amax = absmax_bits8(v[u], amax);
+  for (int u = 0; u < Q; ++u) amax = absmax_bits8(v[u], amax);
   amax = wave_max_u32(amax);
   const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
   const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
 #pragma unroll
-  for (int u = 0; u < kQ; ++u) {
+  for (int u = 0; u < Q; ++u) {
+    if (64u * u >= nchunks) break;        // wave-uniform: no chunk of this batch is in the row
     const uint32_t idx = lane + 64 * u;
     const uint2 q = quant8<F16>(v[u], s, r, zero, exact_div);
     if (idx < nchunks) {
@@ -120,13 +123,14 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
   return s;
 }
 
-// Up to kMaxWaves waves per workgroup: three waves per SIMD.
-template <bool HAS_BIAS, bool TWO, int MODE, bool F16>
+// Up to kMaxWaves waves per workgroup: three waves per SIMD. TB: blocks of 8
+// tokens (1, 2 or 4).
+template <bool HAS_BIAS, int TB, int MODE, bool F16>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
-    float* __restrict__ sa_out, int vec_flags) {
+    float* __restrict__ sa_out, int vec_flags, int G) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
-  __shared__ float sa_lds[16];
+  __shared__ float sa_lds[8 * TB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -135,8 +139,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   const int64_t K = a.K, N = a.N;
   const int ldxs = xs_stride(K);
   const int nwin = (int)((K + 127) / 128);
-  const int64_t n_base = ((int64_t)blockIdx.x * W + wave) * 8;
-  const int rows_valid = (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
+  // waves G.. of the workgroup own no weight rows: they only help quantise
+  const int64_t n_base = ((int64_t)blockIdx.x * G + wave) * 8;
+  const int rows_valid = wave < G ? (int)max<int64_t>(0, min<int64_t>(8, N - n_base)) : 0;
   const uint32_t nchunks = (uint32_t)(K >> 3);
   const bool write_q = blockIdx.x == 0;
 
@@ -222,30 +227,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
       }
     }
     __syncthreads();
+    if (rows_valid == 0) return;
     issue_all();
   }
   if (rows_valid == 0) return;
 
   // ---- 3. weight streaming ----
-  v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+  v4i acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = v4i{0, 0, 0, 0};
   const int8_t* xb = xs + (lane & 7) * ldxs + 16 * chunk;
   // window w: its LDS read(s) and MFMA(s); windows past the end multiply zero
   // weights, so the LDS read is kept inside the row (its last window)
   auto window = [&](int w, const v4i& wv) {
     const int wc = min(w, nwin - 1);
-    const v4i b0 = *reinterpret_cast<const v4i*>(xb + 128 * wc);
-    acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, b0, acc0, 0, 0, 0);
-    if constexpr (TWO) {
-      const v4i b1 = *reinterpret_cast<const v4i*>(xb + 8 * ldxs + 128 * wc);
-      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, b1, acc1, 0, 0, 0);
-    }
+    v4i b[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) b[t] = *reinterpret_cast<const v4i*>(xb + 8 * t * ldxs + 128 * wc);
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wv, b[t], acc[t], 0, 0, 0);
   };
   if constexpr (MODE != LONG) {
 #pragma unroll
     for (int d = 0; d < kD; ++d) {
       window(d, buf[d]);
-      __builtin_amdgcn_sched_group_barrier(0x100, TWO ? 2 : 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
     }
   } else {
     for (int base = 0; base < nwin; base += kD) {
@@ -253,8 +260,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
       for (int d = 0; d < kD; ++d) {
         window(base + d, buf[d]);
         buf[d] = wload(base + d + kD);
-        __builtin_amdgcn_sched_group_barrier(0x100, TWO ? 2 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, TWO ? 2 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     }
@@ -265,12 +272,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   // is D[n][t] + D[n+8][t+8], whose second term is 40 lanes up; lanes 0-7
   // and 16-23 then hold rows nl..nl+3 (nl = 4*(lane/16)) of token lane%8.
   const int src = ((lane + 40) & 63) * 4;
-  v4i s0, s1;
+  v4i sum[TB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s0[r] = acc0[r] + __builtin_amdgcn_ds_bpermute(src, acc0[r]);
-    s1[r] = TWO ? acc1[r] + __builtin_amdgcn_ds_bpermute(src, acc1[r]) : 0;
-  }
+  for (int t = 0; t < TB; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum[t][r] = acc[t][r] + __builtin_amdgcn_ds_bpermute(src, acc[t][r]);
   if ((lane & 8) != 0 || lane >= 32) return;
   const int nl = 4 * (lane >> 4);
   const int64_t n = n_base + nl;
@@ -282,10 +288,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     bb[r] = (HAS_BIAS && ok) ? half_to_f32<F16>(a.bias[n + r]) : 0.f;
   }
 #pragma unroll
-  for (int blk = 0; blk < (TWO ? 2 : 1); ++blk) {
+  for (int blk = 0; blk < TB; ++blk) {
     const int m = 8 * blk + (lane & 7);
     if (m >= M) continue;
-    const v4i c = blk ? s1 : s0;
+    const v4i c = sum[blk];
     const float sa = sa_lds[m];
     uint32_t y[4];
 #pragma unroll
@@ -311,38 +317,50 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <bool HAS_BIAS, bool TWO, bool F16>
+template <bool HAS_BIAS, int TB, bool F16>
 hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   const RowGroupGrid g = row_group_grid(a.N);
-  const dim3 grid(g.blocks), block(64 * g.waves);
-  const size_t lds = (size_t)(TWO ? 16 : 8) * (size_t)xs_stride(a.K);
+  // Four token blocks: kMaxWaves waves quantise the rows whatever the weight
+  // rows per workgroup (g.waves groups), so the per-workgroup quantisation of
+  // up to 32 rows has three waves per SIMD to hide its latency.
+  const int threads = 64 * (TB == 4 ? kMaxWaves : g.waves);
+  const dim3 grid(g.blocks), block(threads);
+  const int G = g.waves;
+  const size_t lds = (size_t)(8 * TB) * (size_t)xs_stride(a.K);
   const int vf = epilogue_vec_flags(a);
   if (a.K > kShortK)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, LONG, F16>), grid, block, lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vf);
-  else if (a.M <= g.waves)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, ONE_ROW, F16>), grid, block, lds, stream, x,
-                       ldx, a, xq_out, a_scale_out, vf);
-  else if (!F16 && a.M <= 2 * g.waves) {
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, LONG, F16>), grid, block, lds, stream, x, ldx,
+                       a, xq_out, a_scale_out, vf, G);
+  else if (TB == 4)
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, SHORT, F16>), grid, block, lds, stream, x, ldx,
+                       a, xq_out, a_scale_out, vf, G);
+  else if (a.M <= g.waves) {
+    if constexpr (TB < 4)
+      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, ONE_ROW, F16>), grid, block, lds, stream, x,
+                         ldx, a, xq_out, a_scale_out, vf, G);
+  } else if (!F16 && a.M <= 2 * g.waves) {
     // (bf16 only: the fp16 instantiation of this mode spills registers)
-    if constexpr (!F16)
-      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, TWO_ROWS, F16>), grid, block, lds, stream,
-                         x, ldx, a, xq_out, a_scale_out, vf);
+    if constexpr (!F16 && TB < 4)
+      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, TWO_ROWS, F16>), grid, block, lds, stream,
+                         x, ldx, a, xq_out, a_scale_out, vf, G);
   } else
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TWO, SHORT, F16>), grid, block, lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vf);
+    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, SHORT, F16>), grid, block, lds, stream, x, ldx,
+                       a, xq_out, a_scale_out, vf, G);
   return hipGetLastError();
 }
 
 template <bool F16>
 hipError_t launch_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                         float* a_scale_out, hipStream_t stream) {
-  if (a.bias)
-    return a.M > 8 ? launch_variant<true, true, F16>(x, ldx, a, xq_out, a_scale_out, stream)
-                   : launch_variant<true, false, F16>(x, ldx, a, xq_out, a_scale_out, stream);
-  return a.M > 8 ? launch_variant<false, true, F16>(x, ldx, a, xq_out, a_scale_out, stream)
-                 : launch_variant<false, false, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  if (a.bias) {
+    if (a.M > 16) return launch_variant<true, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+    return a.M > 8 ? launch_variant<true, 2, F16>(x, ldx, a, xq_out, a_scale_out, stream)
+                   : launch_variant<true, 1, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  }
+  if (a.M > 16) return launch_variant<false, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  return a.M > 8 ? launch_variant<false, 2, F16>(x, ldx, a, xq_out, a_scale_out, stream)
+                 : launch_variant<false, 1, F16>(x, ldx, a, xq_out, a_scale_out, stream);
 }
 
 }  // namespace
@@ -350,6 +368,8 @@ hipError_t launch_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_
 hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
+  if (a.M > kSmallMWideRows || a.K > (a.M > 16 ? kSmallMWideMaxK : kSmallMMaxK))
+    return hipErrorInvalidValue;
   return a.f16 ? launch_dtype<true>(x, ldx, a, xq_out, a_scale_out, stream)
                : launch_dtype<false>(x, ldx, a, xq_out, a_scale_out, stream);
 }

@@ -59,8 +59,11 @@ size_t gemm_partial_bytes(int64_t M, int64_t N, int64_t K);
 
 // Small-M path: per-row activation quantisation on chip + weight-streaming
 // MFMA product + epilogue, one kernel. Also writes xq/a_scale to xq_out /
-// a_scale_out. Needs M <= 16 and K <= kSmallMMaxK.
+// a_scale_out. Needs M <= 16 and K <= kSmallMMaxK, or M <= kSmallMWideRows
+// and K <= kSmallMWideMaxK (the quantised rows are held in LDS).
 constexpr int64_t kSmallMMaxK = 8192;
+constexpr int64_t kSmallMWideRows = 32;
+constexpr int64_t kSmallMWideMaxK = 4096;
 hipError_t launch_small_m(const uint16_t* x, int64_t ldx, const GemmArgs& a,
                           int8_t* xq_out, float* a_scale_out, hipStream_t stream);
 
