@@ -124,9 +124,10 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     bytes, 16-byte aligned, owned by the caller. After the call it holds the
  *     quantised activations xq [M, K] int8 (row stride K) at byte offset 0 and
  *     a_scale [M] fp32 at byte offset W8A8_ALIGN256(M*K), on both paths.
- *     For shapes that keep 256x256 tiles but fill under half of the compute
- *     units with them (N % 8 == 0, K above 896; w8a8_gemm_tile reports the
- *     tile), the size also covers two slices of int32 partial sums after
+ *     For shapes whose 256x256 tiles fill at most half of the compute units,
+ *     or whose 128x128 tiles fill at most one round of them (N % 8 == 0,
+ *     K above 896; w8a8_gemm_tile reports the tile), the size also covers
+ *     two slices of int32 partial sums after
  *     a_scale: the GEMM then splits K in two and a second kernel adds the
  *     partial sums before the epilogue (exact in int32, so the results are
  *     the same bits). The size depends on the current device's compute-unit

@@ -148,7 +148,10 @@ def test_workspace_and_path_queries():
     base = lambda M, K: ((M * K + 255) // 256) * 256 + ((4 * M + 255) // 256) * 256
     assert w8.workspace_bytes(512, 4096, 12288) == base(512, 4096) + 2 * 512 * 12288 * 4
     assert w8.workspace_bytes(700, 2000, 8200) == base(700, 2000) + 2 * 700 * 8200 * 4
-    assert w8.workspace_bytes(512, 4096, 4096) == base(512, 4096)        # 128x128 tiles
+    assert w8.workspace_bytes(512, 4096, 4096) == base(512, 4096) + 2 * 512 * 4096 * 4  # 128 tiles
+    assert w8.workspace_bytes(1024, 4096, 4096) == base(1024, 4096) + 2 * 1024 * 4096 * 4
+    assert w8.workspace_bytes(1024, 4096, 4104) == base(1024, 4096) + 2 * 1024 * 4104 * 4  # 256 tiles
+    assert w8.workspace_bytes(256, 3072, 18432) == base(256, 3072)      # 288 128x128 tiles
     assert w8.workspace_bytes(4352, 3072, 9216) == base(4352, 3072)      # enough tiles
     assert w8.workspace_bytes(512, 4096, 12296) == base(512, 4096) + 2 * 512 * 12296 * 4
     assert w8.workspace_bytes(512, 4096, 12292) == base(512, 4096)       # N % 8 != 0

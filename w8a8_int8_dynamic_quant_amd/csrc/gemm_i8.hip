@@ -495,7 +495,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
   const int vec_flags = epilogue_vec_flags(a);
   if (splits == 1) kps = (int)((a.K + BK - 1) / BK);
   dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * WAVES_M * WAVES_N);
-  if constexpr (BM == 256 && BN == 256) {
+  if constexpr (BM == BN && BM >= 128) {
     if (splits > 1) {         // partial sums only: bias and output type do not matter
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, false, false, true>),
                          grid, block, 0, stream, a, (int)tiles_m, (int)tiles_n, vec_flags, kps);
@@ -516,16 +516,18 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
   return hipGetLastError();
 }
 
-// Split-K plan for a shape: when the tile choice keeps 256x256 tiles but
-// they fill under half of the compute units (and K has at least 8 stages),
-// K is split in two, so twice the workgroups stream panels. More splits lose:
-// each adds a slice of int32 partial sums, written and read back (measured on
-// 512x4096x12288: 58 -> 53-55 us with two; 512x4096x4096 with 8 and
-// 1024x4096x4096 with 4 were slower than 128x128 tiles unsplit, 43 against
-// 41 and 57 against 49 us). splits = 1: no split.
+// Split-K plan for a shape: K is split in two (with K of at least 8 stages)
+// when the chosen tiles leave compute units idle: 256x256 tiles filling at
+// most half of them, or 128x128 tiles filling at most one round (two 64 KiB
+// 128x128 workgroups share a CU, so the split pairs overlap). Measured:
+// 512x4096x12288 (256 tiles) 58 -> 53-55 us; 512x4096x4096 41 -> 31 us,
+// 1024x4096x4096 49 -> 40 us, 512x4096x8192 49 -> 40 us (128 tiles). More
+// splits lose: each adds a slice of int32 partial sums, written and read back
+// (512x4096x4096 split 8 ways on 256 tiles: 43 us). splits = 1: no split.
 struct SplitPlan {
   int splits = 1;
   int kps = 0;              // K stages per split
+  int tile = 256;           // BM = BN of the split GEMM
 };
 
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
@@ -533,10 +535,11 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   if ((N & 7) != 0 || N > (int64_t(1) << 21)) return p;
   int bm, bn;
   gemm_pick_tile(M, N, K, &bm, &bn);
-  if (bm != 256) return p;
-  const int64_t tiles256 = ((M + 255) / 256) * ((N + 255) / 256);
+  if (bm < 128) return p;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t nk = (K + 127) / 128;
-  if (2 * tiles256 >= device_cus() || nk < 8) return p;
+  if ((bm == 128 ? tiles : 2 * tiles) > device_cus() || nk < 8) return p;
+  p.tile = bm;
   p.kps = (int)((nk + 1) / 2);
   p.splits = (int)((nk + p.kps - 1) / p.kps);
   return p;
@@ -572,7 +575,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int vf = epilogue_vec_flags(a);
     const SplitPlan p = split_plan(a.M, a.N, a.K);
     if (p.splits > 1 && (vf & 4) && (!a.acc_debug || (vf & 2))) {
-      if (hipError_t e = launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps);
+      if (hipError_t e = p.tile == 256 ? launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
+                                        : launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps);
           e != hipSuccess)
         return e;
       const int64_t groups = a.M * (a.N >> 3);
