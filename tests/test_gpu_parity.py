@@ -320,15 +320,17 @@ def test_linear_256_tile_store_paths(N, with_bias):
     print(_linear_case(x, w, b)[0])
 
 
-# Split K: shapes whose 256x256 tiles fill at most half of the compute units,
-# or whose 128x128 tiles fill at most one round; w8a8_linear then splits K in
-# two (its workspace holds the
-# partial sums), w8a8_scaled_mm does not. Both must give the oracle's acc and
-# the same y bits. (K = 1040: nine K stages, the second split ends on a
-# 16-byte tail.)
+# Split K: shapes whose 256x256 tiles fill at most half of the compute units
+# or whose 128x128 tiles fill at most one round (K split in two), and skinny
+# shapes on 64x64 tiles (K split in up to four); w8a8_linear then splits K
+# (its workspace holds the partial sums), w8a8_scaled_mm does not. Both must
+# give the oracle's acc and the same y bits. (K = 1040 / 2064: the last split
+# ends on a 16-byte tail.)
 @pytest.mark.parametrize("M,N,K,with_bias", [(512, 12288, 4096, True), (700, 8200, 2000, True),
                                              (520, 10240, 1040, False), (512, 4096, 4096, False),
-                                             (200, 2056, 1040, True), (1024, 2056, 2064, True)])
+                                             (200, 2056, 1040, True), (1024, 2056, 2064, True),
+                                             (64, 18432, 3072, True), (40, 1032, 2064, True),
+                                             (100, 2056, 4096, False)])
 def test_linear_split_k(M, N, K, with_bias):
     assert w8.workspace_bytes(M, K, N) > M * K + 4 * M + 512, "the split path is taken"
     rng = np.random.default_rng(M + N + K)

@@ -495,7 +495,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
   const int vec_flags = epilogue_vec_flags(a);
   if (splits == 1) kps = (int)((a.K + BK - 1) / BK);
   dim3 grid((unsigned)tiles, (unsigned)splits), block(64 * WAVES_M * WAVES_N);
-  if constexpr (BM == BN && BM >= 128) {
+  if constexpr (BM == BN) {
     if (splits > 1) {         // partial sums only: bias and output type do not matter
       hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, WAVES_M, WAVES_N, BK, S, false, false, true>),
                          grid, block, 0, stream, a, (int)tiles_m, (int)tiles_n, vec_flags, kps);
@@ -523,7 +523,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
 // 512x4096x12288 (256 tiles) 58 -> 53-55 us; 512x4096x4096 41 -> 31 us,
 // 1024x4096x4096 49 -> 40 us, 512x4096x8192 49 -> 40 us (128 tiles). More
 // splits lose: each adds a slice of int32 partial sums, written and read back
-// (512x4096x4096 split 8 ways on 256 tiles: 43 us). splits = 1: no split.
+// (512x4096x4096 split 8 ways on 256 tiles: 43 us), except on 64x64 tiles,
+// whose skinny products wait on the weight stream: up to four pieces there
+// (64x3072x18432: 34 -> 30 us in three, 64x4096x4096: 34 -> 19 us in four).
+// splits = 1: no split.
 struct SplitPlan {
   int splits = 1;
   int kps = 0;              // K stages per split
@@ -535,7 +538,18 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   if ((N & 7) != 0 || N > (int64_t(1) << 21)) return p;
   int bm, bn;
   gemm_pick_tile(M, N, K, &bm, &bn);
-  if (bm < 128) return p;
+  if (bm == 64) {
+    // 64x64 tiles (M < 128), latency-bound on the weight stream: up to four
+    // K pieces, so that about four 16 KiB workgroups stream per CU
+    const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t nk = (K + 63) / 64;
+    const int64_t s = std::min<int64_t>(4, (4 * (int64_t)device_cus()) / tiles);
+    if (s < 2 || nk < 8 * s) return p;
+    p.tile = 64;
+    p.kps = (int)((nk + s - 1) / s);
+    p.splits = (int)((nk + p.kps - 1) / p.kps);
+    return p;
+  }
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t nk = (K + 127) / 128;
   if ((bm == 128 ? tiles : 2 * tiles) > device_cus() || nk < 8) return p;
@@ -575,8 +589,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int vf = epilogue_vec_flags(a);
     const SplitPlan p = split_plan(a.M, a.N, a.K);
     if (p.splits > 1 && (vf & 4) && (!a.acc_debug || (vf & 2))) {
-      if (hipError_t e = p.tile == 256 ? launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
-                                        : launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps);
+      if (hipError_t e = p.tile == 256   ? launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
+                         : p.tile == 128 ? launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
+                                         : launch_cfg<64, 64, 2, 2, 64, 2>(a, stream, p.splits, p.kps);
           e != hipSuccess)
         return e;
       const int64_t groups = a.M * (a.N >> 3);
