@@ -127,8 +127,9 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     For shapes whose 256x256 tiles fill at most half of the compute units,
  *     or whose 128x128 tiles fill at most one round of them (N % 8 == 0,
  *     K above 896; w8a8_gemm_tile reports the tile), and for M < 128 with
- *     up to two 64x64 tiles per compute unit (K of at least 1024), the size
- *     also covers two to four slices of int32 partial sums after
+ *     up to two 64x64 tiles per compute unit (K of at least 1024), when the
+ *     shape is not on the small-M path, the size also covers two to four
+ *     slices of int32 partial sums after
  *     a_scale: the GEMM then splits K and a second kernel adds the
  *     partial sums before the epilogue (exact in int32, so the results are
  *     the same bits). The size depends on the current device's compute-unit

@@ -156,6 +156,7 @@ def test_workspace_and_path_queries():
     assert w8.workspace_bytes(64, 4096, 4096) == base(64, 4096) + 4 * 64 * 4096 * 4
     assert w8.workspace_bytes(100, 3072, 18432) == base(100, 3072)      # 576 64x64 tiles
     assert w8.workspace_bytes(40, 960, 1024) == base(40, 960)           # K too short
+    assert w8.workspace_bytes(32, 3072, 18432) == base(32, 3072)        # small-M path
     assert w8.workspace_bytes(4352, 3072, 9216) == base(4352, 3072)      # enough tiles
     assert w8.workspace_bytes(512, 4096, 12296) == base(512, 4096) + 2 * 512 * 12296 * 4
     assert w8.workspace_bytes(512, 4096, 12292) == base(512, 4096)       # N % 8 != 0

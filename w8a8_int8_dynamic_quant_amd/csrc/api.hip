@@ -93,11 +93,11 @@ int linear_common(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const in
                                             W8A8_ALIGN256((size_t)M * (size_t)K));
   hipStream_t st = (hipStream_t)stream;
   w8a8::GemmArgs g{xq, a_scale, wq, w_scale, bias, out, acc_debug, M, N, K, ldo, f16};
+  if (small_m_path(M, K)) return hip_status(w8a8::launch_small_m(x, ldx, g, xq, a_scale, st));
   if (w8a8::gemm_partial_bytes(M, N, K) > 0)       // split-K partial sums follow a_scale
     g.partial = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                            W8A8_ALIGN256((size_t)M * (size_t)K) +
                                            W8A8_ALIGN256((size_t)M * sizeof(float)));
-  if (small_m_path(M, K)) return hip_status(w8a8::launch_small_m(x, ldx, g, xq, a_scale, st));
   if (int s = hip_status(w8a8::launch_quant_rows(x, M, K, ldx, xq, a_scale, st, f16))) return s;
   return hip_status(w8a8::launch_gemm(g, st));
 }
@@ -180,7 +180,8 @@ int w8a8_scaled_mm_f16(const int8_t* xq, const float* a_scale, int64_t M, int64_
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K, int64_t N) {
   if (M <= 0 || K <= 0) return 0;
-  const size_t partial = N > 0 ? w8a8::gemm_partial_bytes(M, N, K) : 0;
+  // the small-M path never splits K
+  const size_t partial = (N > 0 && !small_m_path(M, K)) ? w8a8::gemm_partial_bytes(M, N, K) : 0;
   return W8A8_ALIGN256((size_t)M * (size_t)K) + W8A8_ALIGN256((size_t)M * sizeof(float)) +
          W8A8_ALIGN256(partial);
 }
