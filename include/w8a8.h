@@ -126,8 +126,8 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     a_scale [M] fp32 at byte offset W8A8_ALIGN256(M*K), on both paths.
  *     For shapes whose 256x256 tiles fill at most half of the compute units,
  *     or whose 128x128 tiles fill at most one round of them (N % 8 == 0,
- *     K above 896; w8a8_gemm_tile reports the tile), and for M < 128 with
- *     up to two 64x64 tiles per compute unit (K of at least 1024), when the
+ *     K above 896; w8a8_gemm_tile reports the tile), and for 64x64 tiles
+ *     numbering up to two per compute unit (K of at least 1024), when the
  *     shape is not on the small-M path, the size also covers two to four
  *     slices of int32 partial sums after
  *     a_scale: the GEMM then splits K and a second kernel adds the

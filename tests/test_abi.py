@@ -143,6 +143,11 @@ def test_workspace_and_path_queries():
     assert w8.linear_path(-1, 64, 8) == w8.ERR_INVALID_ARG
     bm, bn = w8.gemm_tile(4352, 3072, 9216)
     assert bm >= 128 and bn >= 128
+    # 65..127 rows: 128x128 tiles when two K pieces of them fill 256 CUs
+    assert w8.gemm_tile(64, 3072, 18432) == (64, 64)
+    assert w8.gemm_tile(65, 3072, 32768) == (128, 128)
+    assert w8.gemm_tile(127, 3072, 16256) == (64, 64)
+    assert w8.gemm_tile(127, 3072, 16384) == (128, 128)
     # split K (on a device of 256 compute units, the count assumed without a
     # GPU): the workspace adds int32 partial sums after xq and a_scale
     base = lambda M, K: ((M * K + 255) // 256) * 256 + ((4 * M + 255) // 256) * 256
@@ -154,7 +159,8 @@ def test_workspace_and_path_queries():
     assert w8.workspace_bytes(256, 3072, 18432) == base(256, 3072)      # 288 128x128 tiles
     assert w8.workspace_bytes(64, 3072, 18432) == base(64, 3072) + 3 * 64 * 18432 * 4
     assert w8.workspace_bytes(64, 4096, 4096) == base(64, 4096) + 4 * 64 * 4096 * 4
-    assert w8.workspace_bytes(100, 3072, 18432) == base(100, 3072)      # 576 64x64 tiles
+    assert w8.workspace_bytes(100, 3072, 18432) == base(100, 3072) + 2 * 100 * 18432 * 4  # 128
+    assert w8.workspace_bytes(100, 3072, 40000) == base(100, 3072)      # 313 128x128 tiles
     assert w8.workspace_bytes(40, 960, 1024) == base(40, 960)           # K too short
     assert w8.workspace_bytes(32, 3072, 18432) == base(32, 3072)        # small-M path
     assert w8.workspace_bytes(4352, 3072, 9216) == base(4352, 3072)      # enough tiles

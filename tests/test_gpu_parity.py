@@ -153,7 +153,8 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None, check_ws=True):
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (4, 100, 8192), (16, 70, 8192),
                                    (2, 129, 8208), (17, 33, 64), (33, 67, 80),
                                    (67, 17, 208), (16, 300, 112), (65, 129, 1040),
-                                   (130, 260, 528), (257, 513, 256), (300, 700, 1296)])
+                                   (130, 260, 528), (257, 513, 256), (300, 700, 1296),
+                                   (65, 33000, 1040), (127, 32776, 64)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_linear_small_shapes(M, N, K, with_bias):
     rng = np.random.default_rng(M * 1000 + N + K)
@@ -330,7 +331,7 @@ def test_linear_256_tile_store_paths(N, with_bias):
                                              (520, 10240, 1040, False), (512, 4096, 4096, False),
                                              (200, 2056, 1040, True), (1024, 2056, 2064, True),
                                              (64, 18432, 3072, True), (40, 1032, 2064, True),
-                                             (100, 2056, 4096, False)])
+                                             (100, 2056, 4096, False), (100, 18432, 3072, True)])
 def test_linear_split_k(M, N, K, with_bias):
     assert w8.workspace_bytes(M, K, N) > M * K + 4 * M + 512, "the split path is taken"
     rng = np.random.default_rng(M + N + K)

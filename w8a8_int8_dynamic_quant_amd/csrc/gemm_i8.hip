@@ -561,7 +561,7 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 
 }  // namespace
 
-// 256x256 tiles, unless 128x128 tiles finish first: a 128x128 tile takes
+// M >= 128: 256x256 tiles, unless 128x128 tiles finish first: a 128x128 tile takes
 // about 0.6 of a 256x256 tile's time on the same K (measured on 512x4096x4096:
 // 40 us in one round of 128 small tiles against 57 us for 32 large ones; on
 // 512x4096x12288, 61 us in two rounds against 58 us in one), so the small
@@ -569,8 +569,18 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 // fewer than the large tiles' rounds.
 void gemm_pick_tile(int64_t M, int64_t N, int64_t K, int* bm, int* bn) {
   (void)K;
-  if (M < 128) { *bm = 64; *bn = 64; return; }
   const int64_t cus = device_cus();
+  if (M <= 64) { *bm = 64; *bn = 64; return; }
+  if (M < 128) {
+    // one 128-row tile reads each weight panel once where two 64-row tiles
+    // read it twice; it pays when two K pieces of such tiles fill the chip
+    // (100x3072x18432: 42 -> 32 us), not on narrow outputs, where 64x64
+    // tiles split four ways keep more workgroups streaming (120x12288x3072:
+    // 35 against 55 us)
+    if (2 * ((N + 127) / 128) >= cus) { *bm = 128; *bn = 128; return; }
+    *bm = 64; *bn = 64;
+    return;
+  }
   const int64_t r256 = (((M + 255) / 256) * ((N + 255) / 256) + cus - 1) / cus;
   const int64_t r128 = (((M + 127) / 128) * ((N + 127) / 128) + cus - 1) / cus;
   if (M >= 512 && N >= 512 && 5 * r256 <= 3 * r128) { *bm = 256; *bn = 256; return; }
