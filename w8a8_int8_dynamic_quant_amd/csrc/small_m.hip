@@ -321,10 +321,10 @@ template <bool HAS_BIAS, int TB, bool F16>
 hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                           float* a_scale_out, hipStream_t stream) {
   const RowGroupGrid g = row_group_grid(a.N);
-  // Four token blocks: kMaxWaves waves quantise the rows whatever the weight
-  // rows per workgroup (g.waves groups), so the per-workgroup quantisation of
-  // up to 32 rows has three waves per SIMD to hide its latency.
-  const int threads = 64 * (TB == 4 ? kMaxWaves : g.waves);
+  // Above 8 rows, kMaxWaves waves quantise the rows whatever the weight rows
+  // per workgroup (g.waves groups), so the per-workgroup quantisation has
+  // three waves per SIMD to hide its latency and spread its VALU work.
+  const int threads = 64 * (TB >= 2 ? kMaxWaves : g.waves);
   const dim3 grid(g.blocks), block(threads);
   const int G = g.waves;
   const size_t lds = (size_t)(8 * TB) * (size_t)xs_stride(a.K);
@@ -335,11 +335,11 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   else if (TB == 4)
     hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, SHORT, F16>), grid, block, lds, stream, x, ldx,
                        a, xq_out, a_scale_out, vf, G);
-  else if (a.M <= g.waves) {
+  else if (a.M <= threads / 64) {
     if constexpr (TB < 4)
       hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, ONE_ROW, F16>), grid, block, lds, stream, x,
                          ldx, a, xq_out, a_scale_out, vf, G);
-  } else if (!F16 && a.M <= 2 * g.waves) {
+  } else if (!F16 && a.M <= 2 * (threads / 64)) {
     // (bf16 only: the fp16 instantiation of this mode spills registers)
     if constexpr (!F16 && TB < 4)
       hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, TWO_ROWS, F16>), grid, block, lds, stream,
