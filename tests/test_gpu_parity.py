@@ -287,15 +287,16 @@ def test_linear_subnormal_scales_and_outputs():
 
 
 @pytest.mark.parametrize("M,N,K", [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040),
-                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088),
+                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088), (13, 18432, 3072),
                                    (17, 70, 1040), (25, 200, 3072), (32, 18432, 3072),
                                    (24, 70, 3088), (32, 33, 4096)])
 def test_linear_small_m_work_splits(M, N, K):
     """Every way the small-M kernel splits the activation rows over its waves
-    (W = 4 waves for N = 33, 70 and 200, 9 for N = 18432): one row per wave
-    (M <= W), two rows per wave held across the weight requests (W < M <=
-    2W), rows quantised before the stream (M > 2W, and every M above 16) and
-    rows longer than the register-resident limit (K > 3072)."""
+    (W = 4 waves for N = 33, 70 and 200 and 9 for N = 18432 up to M = 8, 12
+    from M = 9 on): one row per wave (M <= W), two rows per wave held across
+    the weight requests (W < M <= 16), rows quantised before the stream
+    (every M above 16; fp16 above W, in the fp16 tests) and rows longer than
+    the register-resident limit (K > 3072)."""
     rng = np.random.default_rng(M * 31 + N + K)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)
