@@ -1,4 +1,5 @@
-"""w8a8_linear captured in a HIP graph (torch.cuda.graph) and replayed.
+"""w8a8_linear and the fused GELU producer captured in a HIP graph
+(torch.cuda.graph) and replayed.
 
 Every path (the small-M kernel, quantisation + GEMM, K split on each tile
 size with its reduction kernel) launches only kernels on the caller's stream,
@@ -64,3 +65,37 @@ def test_linear_graph_replays(M, N, K, with_bias):
         ref = w8.linear(xs, wq, sw, b)      # eager, with its own output and workspace
         torch.cuda.synchronize()
         assert np.array_equal(got, host_bits(ref)), f"replay {rep} differs from the eager call"
+
+
+@pytest.mark.parametrize("approximate", ["none", "tanh"])
+def test_gelu_quant_graph_replays(approximate):
+    """The fused GELU + quantisation on its table path (M*K >= 2^22): the
+    table kernel and the quantising kernel replay from the graph."""
+    M, K = 1400, 3072
+    rng = np.random.default_rng(17 if approximate == "none" else 18)
+    z = dev_bf16(random_bf16(rng, (M, K)))
+    announce(f"graph capture of w8a8_gelu_quant_act {approximate} M={M} K={K}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w8.gelu_quant_act(z, approximate, return_y=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = w8.gelu_quant_act(z, approximate, return_y=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        zs = dev_bf16(random_bf16(rng, (M, K)))
+        z.copy_(zs)
+        torch.cuda.synchronize()
+        announce(f"replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.detach().cpu().clone() for o in outs]
+        ref = w8.gelu_quant_act(zs, approximate, return_y=True)
+        torch.cuda.synchronize()
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               (b.view(torch.int16) if b.dtype == torch.bfloat16 else b).cpu()), \
+                f"replay {rep} differs from the eager call"
