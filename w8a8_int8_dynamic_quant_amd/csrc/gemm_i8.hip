@@ -14,20 +14,20 @@
 //   of xq (both K-contiguous, no transpose), so each lane's 16 accumulators
 //   are four runs of four consecutive output columns n of one output row m:
 //   the epilogue stores 8 bytes of bf16 per run.
-// * A workgroup of NW waves computes a BM x BN tile, each wave a WM x WN
-//   sub-tile held as (WN/32)*(WM/32) MFMA blocks of 16 int32 per lane.
-// * K stages of 128 bytes, so every load instruction fetches whole 128-byte
-//   lines (8 rows x 128 B; half-line requests waste HBM bandwidth). Within a
-//   stage, the fragment reads of k-step s+1 are interleaved with the MFMAs of
-//   k-step s.
+// * Two kernels. 256 x 256 tiles run on eight waves that take turns on the
+//   matrix cores (gemm_pp_kernel, 64-byte K stages in a ring of four LDS
+//   buffers; its comment gives the schedule). 128 x 128 and 64 x 64 tiles run
+//   on four waves, each wave a WM x WN sub-tile of (WN/32)*(WM/32) MFMA
+//   blocks, with K stages of 128 bytes (gemm_i8_kernel; within a stage the
+//   fragment reads of k-step s+1 are interleaved with the MFMAs of k-step s).
 // * Panels stream global -> LDS with buffer_load_dwordx4 ... lds (no VGPR
 //   staging, no ds_write). One wave-instruction fills 1 KiB of LDS linearly
 //   by lane; each lane picks the global 16-byte chunk that belongs at its LDS
 //   slot, which realises an XOR swizzle of the 16-byte chunks so that the
 //   ds_read_b128 of 8 consecutive rows hit distinct banks.
-// * An S-stage LDS ring: loads for stage kt+S-1 are issued right after the
-//   barrier of stage kt; one barrier per stage; the wait before it only
-//   counts this stage's loads (exact s_waitcnt vmcnt).
+// * Four-wave kernel: a two-stage LDS ring; loads for stage kt+1 are issued
+//   right after the barrier of stage kt; one barrier per stage; the wait
+//   before it only counts this stage's loads (exact s_waitcnt vmcnt).
 // * Out-of-range rows read as zeros through the buffer descriptor's bound;
 //   K-tail chunks are sent out of bounds, so ragged M, N and K need no branch.
 // * Output stores are non-temporal, so the output does not evict the panels
@@ -450,6 +450,319 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   }
 }
 
+// Epilogue of the eight-wave kernels: the wave's 128 x 64 sub-tile (rows
+// 128 grp.., columns 64 wn.. of the tile), scaled in the fp32 order of the
+// oracle and stored as bf16 (fp16). With 16-byte output rows it is staged in
+// the wave's own 16 KiB of LDS (`region`) and written as whole 128-byte row
+// segments; no other wave touches the region, so no barrier is needed.
+template <bool HAS_BIAS, bool F16, int HALVES = 1>
+__device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (&acc)[2][4],
+                                                 const float* lds_sa, const float* lds_sw,
+                                                 const float* lds_b, int8_t* region, int64_t m0,
+                                                 int64_t n0, uint32_t rows_x, uint32_t rows_w,
+                                                 int grp, int wn, int lane, int vec_flags) {
+  constexpr int FN = 2, FM = 4;
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int64_t N = a.N;
+  const int64_t ldo = a.ldo;
+  const __amdgpu_buffer_rsrc_t r_out =
+      make_rsrc(a.out + m0 * ldo + n0, (uint32_t)(((int64_t)(rows_x - 1) * ldo + rows_w) * 2));
+  float sa[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) sa[j] = lds_sa[128 * grp + 32 * j + frag_row];
+  // visit(nl, ml, y01, y23): four outputs at wave-local column nl, row ml,
+  // for the row blocks jb .. jb+jn-1
+  auto for_each_out = [&](auto&& visit, int jb = 0, int jn = FM) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = 32 * i + 8 * q + 4 * frag_half;
+        const float4 sw4 = *reinterpret_cast<const float4*>(&lds_sw[64 * wn + nl]);
+        float b4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS) {
+          const float4 bb = *reinterpret_cast<const float4*>(&lds_b[64 * wn + nl]);
+          b4[0] = bb.x; b4[1] = bb.y; b4[2] = bb.z; b4[3] = bb.w;
+        }
+#pragma unroll
+        for (int j = jb; j < jb + jn; ++j) {
+          const int ml = 32 * j + frag_row;
+          const v16i& c = acc[i][j];
+          const float t0 = epilogue_f32<HAS_BIAS>(c[4 * q + 0], sa[j], sw4.x, b4[0]);
+          const float t1 = epilogue_f32<HAS_BIAS>(c[4 * q + 1], sa[j], sw4.y, b4[1]);
+          const float t2 = epilogue_f32<HAS_BIAS>(c[4 * q + 2], sa[j], sw4.z, b4[2]);
+          const float t3 = epilogue_f32<HAS_BIAS>(c[4 * q + 3], sa[j], sw4.w, b4[3]);
+          visit(nl, ml, pack_half2<F16>(t0, t1), pack_half2<F16>(t2, t3));
+        }
+      }
+    }
+  };
+  const int row_base = 128 * grp, col_base = 64 * wn;
+  if (vec_flags & 4) {
+    // HALVES passes over 128 / HALVES rows each: rows of 128 bytes in the
+    // region, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7)
+    constexpr int JN = FM / HALVES, ROWS = 32 * JN;
+    const int c = lane & 7;
+    const bool col_ok = col_base + 8 * c < (int)rows_w;
+#pragma unroll
+    for (int h = 0; h < HALVES; ++h) {
+      for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+        const int r = ml - ROWS * h;
+        *reinterpret_cast<v2u*>(region + r * 128 + 16 * ((nl >> 3) ^ ((r >> 1) & 7)) + 8 * frag_half) =
+            (v2u){y01, y23};
+      }, JN * h, JN);
+      __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0): the wave's LDS writes are done
+#pragma unroll 4
+      for (int p = 0; p < ROWS / 8; ++p) {
+        const int r = 8 * p + (lane >> 3);
+        const v4i v = *reinterpret_cast<const v4i*>(region + r * 128 + 16 * (c ^ ((r >> 1) & 7)));
+        const uint32_t o =
+            col_ok ? (uint32_t)((row_base + ROWS * h + r) * ldo + col_base + 8 * c) * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(v, r_out, o, 0, kOutAux);
+      }
+    }
+  } else if (vec_flags & 1) {
+    for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+      const int n = col_base + nl, m = row_base + ml;
+      const uint32_t o = (n < (int)rows_w) ? (uint32_t)(m * ldo + n) * 2u : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b64((v2u){y01, y23}, r_out, o, 0, kOutAux);
+    });
+  } else {
+    for_each_out([&](int nl, int ml, uint32_t y01, uint32_t y23) {
+      const int n = col_base + nl, m = row_base + ml;
+      const uint32_t base = (uint32_t)(m * ldo + n) * 2u;
+      const uint32_t y[4] = {y01 & 0xffffu, y01 >> 16, y23 & 0xffffu, y23 >> 16};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t o = (n + r < (int)rows_w) ? base + 2u * r : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)y[r], r_out, o, 0, kOutAux);
+      }
+    });
+  }
+  if (a.acc_debug) {
+    const __amdgpu_buffer_rsrc_t r_acc =
+        make_rsrc(a.acc_debug + m0 * N + n0, (uint32_t)(((int64_t)(rows_x - 1) * N + rows_w) * 4));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = row_base + 32 * j + frag_row;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = col_base + 32 * i + 8 * q + 4 * frag_half;
+          const uint32_t base = (uint32_t)(m * N + n) * 4u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t o = (n + r < (int)rows_w) ? base + 4u * r : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b32(acc[i][j][4 * q + r], r_acc, o, 0, 0);
+          }
+        }
+      }
+  }
+}
+
+// 256 x 256 tiles with eight waves in two groups that take turns on the
+// matrix cores ("ping-pong"). Waves w and w + 4 share a SIMD; group g = w / 4
+// owns output rows 128g .. 128g+127 of the tile and wave w % 4 of the group
+// owns columns 64(w % 4) .. +63, so each wave holds a 128 x 64 sub-tile
+// (2 x 4 blocks of 32 x 32, 128 accumulators per lane) and two waves fit on
+// a SIMD. K runs in 64-byte stages (32 KiB of panels) through a ring of four
+// LDS buffers; each stage takes two phases separated by workgroup barriers:
+// in one, group 0 runs its 16 MFMAs of the stage from registers while group
+// 1 reads its fragments of the stage into registers; in the next, the roles
+// swap. So on every SIMD one wave issues MFMAs back to back while the other
+// waits on LDS reads, panel loads and barriers. The panel loads of a stage
+// go out from the read phases of both groups (group 0 the W panel, group 1
+// the xq panel, four 1 KiB requests per wave), three stages ahead: the
+// per-CU load path (about 64 bytes per clock) carries a steady half of its
+// capacity, only waves that are not issuing MFMAs wait on it, and a request
+// has about five phases to land. Group 0's epilogue runs alongside group
+// 1's last MFMAs.
+template <bool HAS_BIAS, bool F16, bool SPLIT>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
+                                                        int vec_flags, int kps) {
+  constexpr int BM = 256, BN = 256, BK = 64, KS = BK / 32;
+  constexpr int FN = 2, FM = 4;
+  constexpr int HALF = 256 * BK;             // one panel of a stage: 16 KiB
+  constexpr int LPW = 4;                     // requests per wave per stage (its group's panel)
+
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds2[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds3[2 * HALF];
+  __shared__ __attribute__((aligned(16))) float lds_sa[BM];
+  __shared__ __attribute__((aligned(16))) float lds_sw[BN];
+  __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? BN : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wn = wave & 3;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int64_t M = a.M, N = a.N, K = a.K;
+
+  const uint32_t rows_w = (uint32_t)min<int64_t>(BN, N - n0);
+  const uint32_t rows_x = (uint32_t)min<int64_t>(BM, M - m0);
+  const int kend = (int)min<int64_t>(K, (int64_t)min<int64_t>((int64_t)(blockIdx.y + 1) * kps,
+                                                              (K + BK - 1) / BK) * BK);
+  {
+    const __amdgpu_buffer_rsrc_t r_sa = make_rsrc(a.a_scale + m0, rows_x * 4u);
+    const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(a.w_scale + n0, rows_w * 4u);
+    if (tid < BM)
+      lds_sa[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sa, tid * 4, 0, 0));
+    else
+      lds_sw[tid - BM] =
+          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sw, (tid - BM) * 4, 0, 0));
+    if constexpr (HAS_BIAS) {
+      const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
+      if (tid < BN) lds_b[tid] = half_to_f32<F16>(__builtin_amdgcn_raw_buffer_load_b16(r_b, tid * 2, 0, 0));
+    }
+  }
+
+  // Requests: group 0 loads the W panel, group 1 the xq panel; wave wn of a
+  // group fills rows 64wn .. 64wn+63 of its panel with four 1 KiB requests
+  // (16 rows x 64 B each). Row 64wn + 16u + lane/4 takes 16-byte chunk
+  // lane % 4 of LDS, which holds global chunk (lane % 4) ^ ((row >> 2) & 3),
+  // and (row >> 2) & 3 = (lane >> 4) & 3 for every u.
+  const __amdgpu_buffer_rsrc_t rsrc = grp == 0 ? make_rsrc(a.wq + n0 * K, rows_w * (uint32_t)K)
+                                                : make_rsrc(a.xq + m0 * K, rows_x * (uint32_t)K);
+  const int kc = 16 * ((lane & 3) ^ ((lane >> 4) & 3));
+  const uint32_t lbase = (uint32_t)(64 * wn + (lane >> 2)) * (uint32_t)K + kc;
+  const uint32_t rows16 = 16u * (uint32_t)K;
+  const int pan = grp * HALF + wn * (LPW * 1024);   // this wave's LDS bytes within a stage
+  auto issue_one = [&](int kt, int8_t* st, int u) {
+    const uint32_t k0 = (uint32_t)kt * BK;
+    uint32_t b = lbase;
+    asm volatile("" : "+v"(b));
+    const uint32_t keep = (uint32_t)((kc - (kend - (int)k0)) >> 31);
+    const uint32_t o = ((b + (uint32_t)u * rows16 + k0) & keep) | (kOOB & ~keep);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, st + pan + u * 1024, 16, o, 0, 0, 0);
+  };
+
+  v16i acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = v16i{};
+
+  // fragment address of k-step ks: row frag_row, chunk 2ks + frag_half under
+  // the swizzle c ^ ((row >> 2) & 3), i.e. fb ^ (32 ks)
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  const int fb = frag_row * BK + 16 * (frag_half ^ ((frag_row >> 2) & 3));
+  const int w_row0 = 64 * wn * BK, x_row0 = HALF + 128 * grp * BK;
+
+  v4i fw[KS][FN], fx[KS][FM];
+  auto read_frags = [&](const int8_t* st) {
+    int f = fb;
+    asm volatile("" : "+v"(f));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int8_t* p = st + (f ^ (32 * ks));
+#pragma unroll
+      for (int i = 0; i < FN; ++i) fw[ks][i] = *reinterpret_cast<const v4i*>(p + w_row0 + 32 * BK * i);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) fx[ks][j] = *reinterpret_cast<const v4i*>(p + x_row0 + 32 * BK * j);
+    }
+  };
+  // MFMAs of one stage, back to back at raised priority (a VMEM request in
+  // the MFMA wave's stream would stall it behind the per-CU load queue)
+  auto compute = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[ks][i], fx[ks][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  const int nk_all = (int)((K + BK - 1) / BK);
+  const int kb = (int)blockIdx.y * kps;
+  const int ke = min(nk_all, kb + kps);
+
+  // Every wave runs the same loop body, read(t) | barrier | compute(t) |
+  // barrier, with group 1 one phase behind group 0 (an extra barrier at the
+  // start; group 1 skips the barrier after its last compute), so stage t is
+  // read in phases 2t (group 0) and 2t+1 (group 1). Right after
+  // its fragment reads of stage t, each wave requests its panel's part of
+  // stage t+3 into the buffer that stage t-1 left at the end of phase 2t-1
+  // (group 0 the W panel in phase 2t, group 1 the xq panel in phase 2t+1),
+  // so the loads go out from the waves that are not issuing MFMAs. Every
+  // read phase sends exactly four requests per wave (past the last stage
+  // they read out of bounds: no memory traffic, zeros into a buffer no stage
+  // reads), so both waits are the constant vmcnt(8): a wave's requests of
+  // stage t+1 have landed by the barrier that ends phase 2t+1.
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) issue_one(kb, lds0, u);
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) issue_one(kb + 1, lds1, u);
+#pragma unroll
+  for (int u = 0; u < LPW; ++u) issue_one(kb + 2, lds2, u);
+  wait_vmcnt_lgkm0<2 * LPW>();
+  stage_barrier();
+  if (grp == 1) stage_barrier();
+  auto body = [&](int s, int8_t* st, int8_t* nx3) {
+    read_frags(st);
+#pragma unroll
+    for (int u = 0; u < LPW; ++u) issue_one(s + 3, nx3, u);
+    wait_vmcnt_lgkm0<2 * LPW>();
+    stage_barrier();
+    compute();
+    wait_vmcnt<2 * LPW>();
+    if (grp == 0 || s + 1 < ke) stage_barrier();
+  };
+  // (unrolled by four, so that every access names its buffer)
+  int s = kb;
+  for (; s + 3 < ke; s += 4) {
+    body(s, lds0, lds3);
+    body(s + 1, lds1, lds0);
+    body(s + 2, lds2, lds1);
+    body(s + 3, lds3, lds2);
+  }
+  if (s < ke) body(s, lds0, lds3);
+  if (s + 1 < ke) body(s + 1, lds1, lds0);
+  if (s + 2 < ke) body(s + 2, lds2, lds1);
+  // every request of this wave (the last ones out of bounds) has written LDS
+  wait_vmcnt<0>();
+  __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (SPLIT) {
+    const __amdgpu_buffer_rsrc_t r_p =
+        make_rsrc(a.partial + ((int64_t)blockIdx.y * M + m0) * N + n0,
+                  (uint32_t)(((int64_t)(rows_x - 1) * N + rows_w) * 4));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int ml = 128 * grp + 32 * j + frag_row;
+        const v16i& c = acc[i][j];
+        const v4i run[4] = {c.lo.lo, c.lo.hi, c.hi.lo, c.hi.hi};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = 64 * wn + 32 * i + 8 * q + 4 * frag_half;
+          const uint32_t o = (nl < (int)rows_w) ? (uint32_t)(ml * N + nl) * 4u : kOOB;
+          __builtin_amdgcn_raw_buffer_store_b128(run[q], r_p, o, 0, 0);
+        }
+      }
+    return;
+  }
+  // Staging, 8 KiB per wave (half the sub-tile at a time), in a buffer that
+  // no request still in flight targets. With n = ke - kb stages, the last
+  // requests (of stages n, n+1, n+2, relative to kb) target buffers
+  // (n-4) .. (n-2) mod 4, never (n-1) mod 4, and no stage is read after group
+  // 0's last barrier: group 0 stages in buffer (n-1) mod 4. Group 1 stages
+  // after draining its own requests and group 0's last barrier, by which
+  // group 0's requests of stage n (buffer n mod 4) have landed: buffer n mod 4.
+  const int n_st = ke - kb;
+  const int pick = grp == 0 ? ((n_st - 1) & 3) : (n_st & 3);
+  int8_t* const stage_buf = pick == 0 ? lds0 : pick == 1 ? lds1 : pick == 2 ? lds2 : lds3;
+  gemm_pp_epilogue<HAS_BIAS, F16, 2>(a, acc, lds_sa, lds_sw, lds_b, stage_buf + wn * 8192, m0, n0,
+                                     rows_x, rows_w, grp, wn, lane, vec_flags);
+}
+
 // Split K, second step: out[m, n..n+7] = epilogue(sum over the slices of
 // the int32 partial sums), in the GEMM epilogue's fp32 order; one thread per
 // eight columns (N % 8 == 0, out rows 16-byte aligned). The int32 sum is
@@ -513,6 +826,33 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
     else W8A8_GEMM(false, false);
   }
 #undef W8A8_GEMM
+  return hipGetLastError();
+}
+
+// 256 x 256 tiles: the eight-wave ping-pong kernel (kps counts 128-byte
+// stages, as the split-K plan does).
+hipError_t launch_pp(const GemmArgs& a, hipStream_t stream, int splits = 1, int kps = 0) {
+  constexpr int T = 256, BK = 64;
+  const int64_t tiles_m = (a.M + T - 1) / T, tiles_n = (a.N + T - 1) / T;
+  const int vec_flags = epilogue_vec_flags(a);
+  kps = splits == 1 ? (int)((a.K + BK - 1) / BK) : 2 * kps;
+  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
+  if (splits > 1) {
+    hipLaunchKernelGGL((gemm_pp_kernel<false, false, true>), grid, block, 0, stream, a,
+                       (int)tiles_m, (int)tiles_n, vec_flags, kps);
+    return hipGetLastError();
+  }
+#define W8A8_PP(B, H)                                                                           \
+  hipLaunchKernelGGL((gemm_pp_kernel<B, H, false>), grid, block, 0, stream, a, (int)tiles_m, \
+                     (int)tiles_n, vec_flags, kps)
+  if (a.f16) {
+    if (a.bias) W8A8_PP(true, true);
+    else W8A8_PP(false, true);
+  } else {
+    if (a.bias) W8A8_PP(true, false);
+    else W8A8_PP(false, false);
+  }
+#undef W8A8_PP
   return hipGetLastError();
 }
 
@@ -599,7 +939,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int vf = epilogue_vec_flags(a);
     const SplitPlan p = split_plan(a.M, a.N, a.K);
     if (p.splits > 1 && (vf & 4) && (!a.acc_debug || (vf & 2))) {
-      if (hipError_t e = p.tile == 256   ? launch_cfg<256, 256, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
+      if (hipError_t e = p.tile == 256   ? launch_pp(a, stream, p.splits, p.kps)
                          : p.tile == 128 ? launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
                                          : launch_cfg<64, 64, 2, 2, 64, 2>(a, stream, p.splits, p.kps);
           e != hipSuccess)
@@ -623,7 +963,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
   one.partial = nullptr;
   int bm, bn;
   gemm_pick_tile(a.M, a.N, a.K, &bm, &bn);
-  if (bm == 256) return launch_cfg<256, 256, 2, 2, 128, 2>(one, stream);
+  if (bm == 256) return launch_pp(one, stream);
   if (bm == 128) return launch_cfg<128, 128, 2, 2, 128, 2>(one, stream);
   return launch_cfg<64, 64, 2, 2, 64, 2>(one, stream);
 }
