@@ -31,6 +31,7 @@ from .w8a8_oracle import (  # noqa: F401
     scale_to_f32,
     w8a16_acc,
     w8a16_abs_sum,
+    w8a16_err_bound,
     w8a16_linear,
     f64_to_bf16_bits,
     layernorm_modulate,

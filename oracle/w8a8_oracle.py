@@ -348,6 +348,27 @@ def w8a16_abs_sum(x_bits, wq, dtype: str = "bf16") -> np.ndarray:
     return x @ np.abs(np.asarray(wq, np.float64)).T
 
 
+def w8a16_err_bound(x_bits, wq, s_w, dtype: str = "bf16") -> np.ndarray:
+    """Bound on |t_kernel - t| for t = fl32(fl32(acc) * s_w) (+ bias), where
+    the kernel accumulates acc in fp32 and this oracle rounds the exact sum
+    once. Reading of the accumulation (the page names the scheme, not its
+    arithmetic): two fp32 accumulators per output (the even and the odd
+    16-element chunks of K) each take 2 * ceil(K / 128) additions of a
+    32-product partial dot, and one addition joins them, so a product meets
+    n = 2 * ceil(K / 128) + 1 sequential roundings after its partial dot; the
+    partial dot of 32 exact products rounds each of them at most 8 times. The
+    standard summation bound then gives gamma_{n+8} * sum|x * wq| with
+    gamma_j ~ j * 2^-24; (2n + 8) * 2^-24 * sum|x * wq| also covers the
+    oracle's own rounding of the exact sum to fp32, and the bound scales with
+    |s_w| through the (monotone) fp32 product. A parity test adds one unit in
+    the last place of the output type, where a rounding boundary may fall
+    between the two values."""
+    K = np.asarray(x_bits).shape[1]
+    n = 2 * ((K + 127) // 128) + 1
+    return (2 * n + 8) * 2.0**-24 * w8a16_abs_sum(x_bits, wq, dtype) * np.abs(
+        np.asarray(s_w, np.float64))[None, :]
+
+
 def w8a16_linear(x_bits, wq, s_w, bias_bits=None, dtype: str = "bf16") -> dict:
     """W8A16 linear: x [M,K] (bf16, or fp16 with dtype='f16'), int8 wq [N,K],
     fp32 s_w [N] -> y bits of the type of x (bias has that type too).

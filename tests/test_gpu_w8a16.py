@@ -39,10 +39,8 @@ def _ulp(v, dtype="bf16"):
 
 
 def check_w8a16(x_bits, wq, sw, bias_bits, y_bits, dtype="bf16") -> dict:
-    K = x_bits.shape[1]
     exp = oracle.w8a16_linear(x_bits, wq, sw, bias_bits, dtype)
-    steps = 2 * ((K + 127) // 128) + 1
-    err = (2 * steps + 8) * 2.0**-24 * oracle.w8a16_abs_sum(x_bits, wq, dtype) * np.abs(sw)[None, :]
+    err = oracle.w8a16_err_bound(x_bits, wq, sw, dtype)
     y = oracle.to_f32(y_bits, dtype).astype(np.float64)
     ye = oracle.to_f32(exp["y"], dtype).astype(np.float64)
     assert np.all(np.isfinite(ye)), "the cases stay inside the output range"
