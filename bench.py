@@ -11,10 +11,11 @@ time); inputs are synthetic (seeded, see synth_inputs) and resident in HBM.
 Prints one JSON line. `value` is int8 TOPS of the whole step (wall clock
 over the timed steps); per-shape figures, the roofline of the dominant kernel
 (the GEMM, bound by int8 MFMA throughput) and the CPU oracle's rate on the
-same step ride along. Inside the timed region HIP events bracket only the
-GEMM launches (an event record costs GPU time); the full per-launch
-breakdown comes from a separate pass after it, then a 2.5 s clock pass reads
-the graphics clock and socket power the chip sustains on the step (`sclk`).
+same step ride along. Inside the timed region HIP events, recorded with a
+device-scope release (hipEventReleaseToDevice), bracket only the GEMM
+launches; the full per-launch breakdown comes from a separate pass after it,
+then a 2.5 s clock pass reads the graphics clock and socket power the chip
+sustains on the step (`sclk`).
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--no-cpu-baseline]
                     [--no-next-rows]
@@ -22,6 +23,7 @@ the graphics clock and socket power the chip sustains on the step (`sclk`).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -35,8 +37,49 @@ sys.path.insert(0, ROOT)
 METRIC = ("int8 TOPS + % of MI355X int8 MFMA peak (HBM GB/s for M≤16), per shape")
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-GEMM_KERNEL = "gemm_i8_kernel"
+GEMM_KERNEL = "gemm_pp_kernel"          # the 256x256-tile kernel all four DiT shapes take
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_i8_dit_block_counters.json")
+
+
+class HipEvents:
+    """Timing events of the HIP runtime that torch and libw8a8 share (one
+    runtime per process: both resolve libamdhip64.so.7 to torch's copy),
+    created with hipEventReleaseToDevice: recording one releases at device
+    scope only, so it does not write the caches back to memory the way a
+    default (system-scope) event does, and the kernels between two events are
+    timed without that cost."""
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self):
+        ev = ctypes.c_void_p()
+        if self.h.hipEventCreateWithFlags(ctypes.byref(ev), self.RELEASE_TO_DEVICE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.made.append(ev)
+        return ev
+
+    def record(self, ev, stream) -> None:
+        if self.h.hipEventRecord(ev, ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b) -> float:
+        t = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(t), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(t.value)
+
+    def close(self) -> None:
+        for ev in self.made:
+            self.h.hipEventDestroy(ev)
+        self.made.clear()
 
 
 def parse():
@@ -71,6 +114,10 @@ def copy_calibration(mib: int) -> None:
 GEMM_SOURCES = ("gemm_i8.hip", "w8a8_device.h", "w8a8_kernels.h")
 
 
+def align256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
 def kernel_source_hash() -> str:
     csrc = os.path.join(ROOT, "w8a8_int8_dynamic_quant_amd", "csrc")
     h = hashlib.sha256()
@@ -80,17 +127,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(gemm_launch_ops):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
-    or None when the kernels changed since the counters were taken."""
+def load_counters():
+    """The committed rocprofv3 summary of the GEMM on this step (HBM bytes and
+    kernel-trace duration per launch), or {} when the kernel sources changed
+    since it was taken."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if c.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return c.get("hbm_bytes_per_launch_avg")
+        return {}
+    return c
 
 
 def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
@@ -120,15 +168,30 @@ def cpu_baseline(inputs, wq_host, min_seconds: float = 10.0):
     return {
         "value": ops / dt / 1e12,
         "unit": "TOPS",
-        "cores": threads or os.cpu_count(),
+        # the oracle's matrix products run on the BLAS threads; the rest of it
+        # (quantisation, epilogue) is single-threaded numpy
+        "cores": threads or 1,
+        "blas_threads": threads,
+        "host_cpus": os.cpu_count(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{steps} whole step(s): the 4 DiT block linears at M=4352 and the M=1 "
                   "modulation projection (quantise, exact int GEMM, fp32 epilogue)",
         "seconds": dt,
-        "host_cpus": os.cpu_count(),
-        "cpu_model": platform.processor() or platform.machine(),
         "numpy": np.__version__,
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def clock_pass(step, torch, seconds: float = 2.5):
@@ -313,8 +376,8 @@ def baseline_configs(w8, torch, dev, to_dev, timed, ok) -> dict:
     """The whole linear (w8a8_linear) on the other configurations of the
     workload table: the probe shapes (64x256x128 with bias, 512x4096x4096
     with outlier channels, 512x4096x12288 Student-t with bias) and the
-    modulation projection at M = 2, 17, 32 (M = 17 and 32 take the GEMM
-    path). Weights rotate over copies totalling more than 512 MB; algorithmic
+    modulation projection at M = 2, 17, 32 (all three on the fused small-M
+    kernel). Weights rotate over copies totalling more than 512 MB; algorithmic
     bytes 2MK + NK + 4N (+ 2N bias) + 2MN."""
     from synth_inputs import make_linear_inputs
     lib = w8.lib()
@@ -455,9 +518,18 @@ def main():
             "out": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
             "ws": torch.empty((w8.workspace_bytes(M, K, N),), dtype=torch.uint8, device=dev),
             "path": w8.linear_path(M, K, N),
+            # w8a8_linear on the GEMM path launches the quantisation and then
+            # the product, exactly the two entry points below, unless it
+            # splits K (a workspace larger than xq + a_scale): time such a
+            # layer through w8a8_linear itself
+            "two_call": (w8.linear_path(M, K, N) == w8.PATH_GEMM and
+                         w8.workspace_bytes(M, K, N) == align256(M * K) + align256(4 * M)),
         })
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+
+    hev = HipEvents()
+    sp = stream.cuda_stream
 
     def step(gemm_events=None, all_events=None):
         """One pass over the block. gemm_events[i] = (start, end) bracket the
@@ -465,52 +537,51 @@ def main():
         quantisation (a..b) and GEMM or fused small-M kernel (b..c)."""
         for i, L in enumerate(layers):
             e = all_events[i] if all_events is not None else None
-            if L["path"] == w8.PATH_GEMM:
+            if L["two_call"]:
                 # w8a8_linear on this path launches exactly these two kernels;
                 # calling the two entry points lets events bracket each one.
                 if e is not None:
-                    e[0].record(stream)
+                    hev.record(e[0], sp)
                 st = w8.lib().w8a8_quant_act(
                     L["x"].data_ptr(), L["M"], L["K"], L["K"], L["xq"].data_ptr(),
-                    L["sa"].data_ptr(), stream.cuda_stream)
+                    L["sa"].data_ptr(), sp)
                 if e is not None:
-                    e[1].record(stream)
+                    hev.record(e[1], sp)
                 if gemm_events is not None:
-                    gemm_events[i][0].record(stream)
+                    hev.record(gemm_events[i][0], sp)
                 st |= w8.lib().w8a8_scaled_mm(
                     L["xq"].data_ptr(), L["sa"].data_ptr(), L["M"], L["K"], L["wq"].data_ptr(),
                     L["sw"].data_ptr(), L["N"],
                     None if L["bias"] is None else L["bias"].data_ptr(),
-                    L["out"].data_ptr(), L["N"], None, stream.cuda_stream)
+                    L["out"].data_ptr(), L["N"], None, sp)
                 if gemm_events is not None:
-                    gemm_events[i][1].record(stream)
+                    hev.record(gemm_events[i][1], sp)
                 if e is not None:
-                    e[2].record(stream)
+                    hev.record(e[2], sp)
             else:
                 if e is not None:
-                    e[0].record(stream)
-                    e[1].record(stream)
+                    hev.record(e[0], sp)
+                    hev.record(e[1], sp)
                 st = w8.lib().w8a8_linear(
                     L["x"].data_ptr(), L["M"], L["K"], L["K"], L["wq"].data_ptr(),
                     L["sw"].data_ptr(), L["N"],
                     None if L["bias"] is None else L["bias"].data_ptr(),
-                    L["out"].data_ptr(), L["N"], L["ws"].data_ptr(), L["ws"].numel(), None,
-                    stream.cuda_stream)
+                    L["out"].data_ptr(), L["N"], L["ws"].data_ptr(), L["ws"].numel(), None, sp)
                 if e is not None:
-                    e[2].record(stream)
+                    hev.record(e[2], sp)
             if st != 0:
                 raise RuntimeError(f"{L['name']}: libw8a8 status {st}")
 
     def new_events(n):
-        return [tuple(torch.cuda.Event(enable_timing=True) for _ in range(n)) for _ in layers]
+        return [tuple(hev.new() for _ in range(n)) for _ in layers]
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: events bracket only the GEMM launches (each event record
-    # costs GPU time; these are the ones the roofline needs).
+    # Timed region: events (device-scope release) bracket only the GEMM
+    # launches, the ones the roofline needs.
     gev = [new_events(2) for _ in range(args.steps)]
     print("[bench] timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -537,8 +608,8 @@ def main():
     gemm_ops = gemm_ms = 0.0
     gemm_launches = 0
     for i, L in enumerate(layers):
-        qs = [aev[s][i][0].elapsed_time(aev[s][i][1]) for s in range(n_bd)]
-        ks = [aev[s][i][1].elapsed_time(aev[s][i][2]) for s in range(n_bd)]
+        qs = [hev.ms(aev[s][i][0], aev[s][i][1]) for s in range(n_bd)]
+        ks = [hev.ms(aev[s][i][1], aev[s][i][2]) for s in range(n_bd)]
         q_ms, k_ms = float(np.mean(qs)), float(np.mean(ks))
         tot = q_ms + k_ms
         M, K, N = L["M"], L["K"], L["N"]
@@ -551,9 +622,8 @@ def main():
                "gbs": alg_bytes / (tot * 1e-3) / 1e9,
                "pct_hbm": 100 * alg_bytes / (tot * 1e-3) / 1e9 / PEAK_HBM_GBS,
                "us_median": float(np.median(np.add(qs, ks))) * 1e3}
-        if L["path"] == w8.PATH_GEMM:
-            g_ms = float(np.mean([gev[s][i][0].elapsed_time(gev[s][i][1])
-                                  for s in range(args.steps)]))
+        if L["two_call"]:
+            g_ms = float(np.mean([hev.ms(gev[s][i][0], gev[s][i][1]) for s in range(args.steps)]))
             row["quant_us"] = q_ms * 1e3
             row["quant_gbs"] = (3 * M * K + 4 * M) / (q_ms * 1e-3) / 1e9
             row["gemm_us"] = g_ms * 1e3
@@ -564,7 +634,9 @@ def main():
             gemm_launches += 1
         per_shape.append(row)
 
+    hev.close()
     achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    counters = load_counters()
     roofline = {
         "bound": "mfma",
         "kernel": GEMM_KERNEL,
@@ -572,10 +644,20 @@ def main():
         "peak": PEAK_INT8_TOPS,
         "unit": "TOPS",
         "frac": achieved / PEAK_INT8_TOPS,
-        "traffic": load_traffic(gemm_ops / gemm_launches),
+        "traffic": counters.get("hbm_bytes_per_launch_avg"),
         "avg_launch_us": gemm_ms * 1e3 / gemm_launches,
         "ops_per_launch_avg": gemm_ops / gemm_launches,
+        "timing": "hipEventReleaseToDevice events around each GEMM launch in the timed region",
     }
+    if counters.get("kernel_trace_avg_us"):
+        # the same kernel's average duration in the committed rocprofv3
+        # kernel trace of this step (no events in that run)
+        kt = counters["kernel_trace_avg_us"]
+        roofline["kernel_trace"] = {"avg_launch_us": kt,
+                                    "achieved": gemm_ops / gemm_launches / (kt * 1e-6) / 1e12,
+                                    "frac": gemm_ops / gemm_launches / (kt * 1e-6) / 1e12 /
+                                    PEAK_INT8_TOPS,
+                                    "source": os.path.relpath(COUNTERS_FILE, ROOT)}
     if sclk is not None:
         # the published peak is quoted at 2.4 GHz; the same MFMA rate at the
         # clock the chip sustained on this step

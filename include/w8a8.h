@@ -34,6 +34,12 @@
  *   inputs, and only enqueues work on `stream` (a hipStream_t passed as
  *   void*; NULL = the default stream). A call returns once the work is
  *   enqueued; the caller keeps every buffer alive until the stream has run it.
+ * - One exception to "no state": a file-scope device array of 256 KiB, the
+ *   lookup table of w8a8_gelu_quant_act (bf16 z -> bf16 GELU(z), one table
+ *   per form). Each GPU the library runs on holds it until the process ends.
+ *   A table-path call rewrites it on the caller's stream before using it,
+ *   always with the same values, so calls on different streams only ever
+ *   write identical bytes and no call depends on an earlier one.
  * - Layouts are row-major. bf16 values are passed as uint16_t bit patterns.
  * - Arguments are validated before anything is launched; on an error nothing
  *   is enqueued and an error status is returned (no exceptions, no abort).
@@ -188,12 +194,14 @@ int w8a8_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  *   wq       [N, K] int8, row stride K (written): q = stored byte - 128
  *   w_scale  [N] fp32 (written; every input type converts exactly)
  * The result feeds w8a8_linear / w8a8_scaled_mm like the output of
- * w8a8_quantize_weights. Requirements: 16 <= K <= W8A8_K_MAX, K % 16 == 0,
- * ldp >= K/4 and ldp % 4 == 0 (else W8A8_ERR_UNSUPPORTED / INVALID_ARG);
- * packed and wq 16-byte aligned. A stored byte 0 gives q = -128, which the
- * symmetric quantiser never produces; with such weights the int32-safe K is
- * 132 104 (127 * 128 * K < 2^31) rather than W8A8_K_MAX.
+ * w8a8_quantize_weights. Requirements: 16 <= K <= W8A8_K_MAX_PACKED, K % 16
+ * == 0, ldp >= K/4 and ldp % 4 == 0 (else W8A8_ERR_UNSUPPORTED /
+ * INVALID_ARG); packed and wq 16-byte aligned. A stored byte 0 gives q = -128,
+ * which the symmetric quantiser never produces; with such weights the
+ * int32-safe K is W8A8_K_MAX_PACKED (127 * 128 * K < 2^31) rather than
+ * W8A8_K_MAX, so longer rows are refused with W8A8_ERR_UNSUPPORTED.
  */
+#define W8A8_K_MAX_PACKED 132104
 #define W8A8_SCALE_F32 0
 #define W8A8_SCALE_BF16 1
 #define W8A8_SCALE_F16 2

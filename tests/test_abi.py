@@ -196,6 +196,11 @@ def test_unpack_validation():
     assert call(scale=P(A + 2)) == w8.ERR_MISALIGNED     # fp32 scales need 4 bytes
     assert call(N=0, packed=None, scale=None, wq=None, ws=None) == w8.OK
     assert f"#define W8A8_SCALE_BF16 {w8.SCALE_BF16}" in open(HEADER).read()
+    # weights that may hold -128: 127 * 128 * K must stay below 2^31
+    assert f"#define W8A8_K_MAX_PACKED {w8.K_MAX_PACKED}" in open(HEADER).read()
+    assert 127 * 128 * w8.K_MAX_PACKED < 2**31 <= 127 * 128 * (w8.K_MAX_PACKED + 1)
+    for K in (132112, w8.K_MAX - w8.K_MAX % 16):
+        assert call(K=K, ldp=K // 4 + (-(K // 4)) % 4) == w8.ERR_UNSUPPORTED, K
 
 
 def test_w8a16_validation():
@@ -289,6 +294,38 @@ def test_gelu_validation():
     assert f"#define W8A8_GELU_ERF {w8.GELU_ERF}" in text
     assert f"#define W8A8_GELU_TANH {w8.GELU_TANH}" in text
     assert w8.PRODUCER_MAX_K["gelu"] == 32768
+
+
+def test_launch_failure_reports_hip_error():
+    """A call that passes validation but whose launch fails returns
+    W8A8_ERR_HIP and records the hipError_t for w8a8_last_hip_error (here
+    the launch fails because no device is visible); the caller can then fall
+    back with the logged reason (unsloth test_diffusion_transformer_quant.py
+    commit log: a quantisation failure falls back, with the reason logged)."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes, sys\n"
+        "L = ctypes.CDLL(sys.argv[1])\n"
+        "P, I = ctypes.c_void_p, ctypes.c_int64\n"
+        "L.w8a8_quant_act.argtypes = [P, I, I, I, P, P, P]\n"
+        "L.w8a8_linear.argtypes = [P, I, I, I, P, P, I, P, P, I, P, ctypes.c_size_t, P, P]\n"
+        "L.w8a8_linear_workspace_bytes.restype = ctypes.c_size_t\n"
+        "L.w8a8_linear_workspace_bytes.argtypes = [I, I, I]\n"
+        "a = 0x10000\n"
+        "s1 = L.w8a8_quant_act(a, 4, 64, 64, a, a, None)\n"
+        "e1 = L.w8a8_last_hip_error()\n"
+        "ws = L.w8a8_linear_workspace_bytes(64, 256, 128)\n"
+        "s2 = L.w8a8_linear(a, 64, 256, 256, a, a, 128, None, a, 128, a, ws, None, None)\n"
+        "print(s1, e1, s2, L.w8a8_last_hip_error())\n")
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    r = subprocess.run([sys.executable, "-c", code, w8.LIB_PATH], env=env,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    s1, e1, s2, e2 = map(int, r.stdout.split()[-4:])
+    assert (s1, s2) == (w8.ERR_HIP, w8.ERR_HIP)
+    assert e1 != 0 and e2 != 0
+    assert w8.status_string(s1) == "HIP launch failed"
 
 
 def test_status_strings():

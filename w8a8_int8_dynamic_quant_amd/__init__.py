@@ -33,6 +33,7 @@ ERR_MISALIGNED = -3
 ERR_WORKSPACE = -4
 ERR_HIP = -5
 K_MAX = 133144
+K_MAX_PACKED = 132104   # ingest: weights may hold -128
 SMALL_M = 16          # small-M path for K <= 8192
 SMALL_M_WIDE = 32     # ... and up to this M for K <= 4096
 LDO_MAX = 1 << 22

@@ -221,6 +221,7 @@ int w8a8_unpack_pack_quantized(const int32_t* packed, int64_t N, int64_t K, int6
                                void* stream) {
   if (N < 0) return W8A8_ERR_INVALID_ARG;
   if (int s = check_k(K)) return s;
+  if (K > W8A8_K_MAX_PACKED) return W8A8_ERR_UNSUPPORTED;   // q = -128 needs the tighter bound
   if (ldp < K / 4) return W8A8_ERR_INVALID_ARG;
   if (ldp % 4 != 0) return W8A8_ERR_UNSUPPORTED;
   if (scale_dtype != W8A8_SCALE_F32 && scale_dtype != W8A8_SCALE_BF16 &&
