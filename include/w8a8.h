@@ -34,12 +34,14 @@
  *   inputs, and only enqueues work on `stream` (a hipStream_t passed as
  *   void*; NULL = the default stream). A call returns once the work is
  *   enqueued; the caller keeps every buffer alive until the stream has run it.
- * - One exception to "no state": a file-scope device array of 256 KiB, the
- *   lookup table of w8a8_gelu_quant_act (bf16 z -> bf16 GELU(z), one table
- *   per form). Each GPU the library runs on holds it until the process ends.
- *   A table-path call rewrites it on the caller's stream before using it,
- *   always with the same values, so calls on different streams only ever
- *   write identical bytes and no call depends on an earlier one.
+ * - Two file-scope device arrays are the exceptions to "no state"; each GPU
+ *   the library runs on holds them until the process ends:
+ *   - the 256 KiB lookup table of w8a8_gelu_quant_act (bf16 z -> bf16
+ *     GELU(z), one table per form). A table-path call rewrites it on the
+ *     caller's stream before using it, always with the same values, so calls
+ *     on different streams only ever write identical bytes and no call
+ *     depends on an earlier one;
+ *   - the 64 MiB scratch of w8a8_linear_noalloc (see there).
  * - Layouts are row-major. bf16 values are passed as uint16_t bit patterns.
  * - Arguments are validated before anything is launched; on an error nothing
  *   is enqueued and an error status is returned (no exceptions, no abort).
@@ -155,6 +157,32 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                 int32_t* acc_debug, void* stream);
 
 #define W8A8_ALIGN256(b) ((((size_t)(b)) + 255u) & ~(size_t)255u)
+
+/*
+ * w8a8_linear for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same layer, the same kernels and bits, with the workspace taken from a
+ * file-scope device array of W8A8_NOALLOC_SCRATCH_BYTES (64 MiB) instead of
+ * the caller. The caller still passes x, the weights, out and acc_debug.
+ * - Each GPU the library runs on holds its own copy of the array until the
+ *   process ends; the first call on a device looks up the array's address on
+ *   that device (hipGetSymbolAddress) and keeps it.
+ * - No call allocates or frees memory (no hipMalloc, no hipFree, no
+ *   allocating library routine).
+ * - Every call on one GPU shares that GPU's array and leaves its contents
+ *   behind (xq at byte offset 0, a_scale at W8A8_ALIGN256(M*K)): calls whose
+ *   work overlaps on one GPU (different streams, or host threads) race on it
+ *   and must be serialised by the caller. Nothing in it needs clearing: every
+ *   byte a call reads, the same call writes first.
+ * - Shapes whose w8a8_linear_workspace_bytes(M, K, N) exceeds the array are
+ *   refused with W8A8_ERR_WORKSPACE (every 1024 px DiT block linear fits);
+ *   other requirements and errors as w8a8_linear.
+ */
+#define W8A8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int w8a8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        const int8_t* wq, const float* w_scale, int64_t N,
+                        const uint16_t* bias, uint16_t* out, int64_t ldo,
+                        int32_t* acc_debug, void* stream);
 
 /*
  * fp16 variants ("Int8 Quantization" guide, "Overview": bf16 and fp16 weights

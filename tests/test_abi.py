@@ -296,6 +296,37 @@ def test_gelu_validation():
     assert w8.PRODUCER_MAX_K["gelu"] == 32768
 
 
+def test_linear_noalloc_validation():
+    """Arguments are checked as w8a8_linear checks them, and shapes whose
+    workspace would exceed the library's scratch array are refused, all
+    before anything touches a device."""
+    f = "w8a8_linear_noalloc"
+    base = [P(A), 8, 64, 64, P(A), P(A), 16, None, P(A), 16, None, None]
+    names = ["x", "M", "K", "ldx", "wq", "ws", "N", "bias", "out", "ldo", "acc", "st"]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(f, *a)
+
+    assert call(M=-1) == w8.ERR_INVALID_ARG
+    assert call(N=0) == w8.ERR_INVALID_ARG
+    assert call(K=40, ldx=40) == w8.ERR_UNSUPPORTED
+    assert call(ldx=48) == w8.ERR_INVALID_ARG
+    assert call(ldo=8) == w8.ERR_INVALID_ARG
+    assert call(x=None) == w8.ERR_INVALID_ARG
+    assert call(wq=None) == w8.ERR_INVALID_ARG
+    assert call(out=None) == w8.ERR_INVALID_ARG
+    assert call(x=P(A + 8)) == w8.ERR_MISALIGNED
+    assert call(M=0, x=None, wq=None, ws=None, out=None) == w8.OK
+    assert f"#define W8A8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in open(HEADER).read()
+    # the largest DiT block activation (4352 x 12288) fits; 8192 x 8192 does not
+    assert w8.workspace_bytes(4352, 12288, 3072) <= w8.NOALLOC_SCRATCH_BYTES
+    assert w8.workspace_bytes(8192, 8192, 64) > w8.NOALLOC_SCRATCH_BYTES
+    assert call(M=8192, K=8192, ldx=8192, N=64, ldo=64) == w8.ERR_WORKSPACE
+
+
 def test_launch_failure_reports_hip_error():
     """A call that passes validation but whose launch fails returns
     W8A8_ERR_HIP and records the hipError_t for w8a8_last_hip_error (here

@@ -8,6 +8,7 @@ there is no fallback.
 
     wq, w_scale = quantize_weights(w)              # load time, bf16/fp16 [N, K]
     y = linear(x, wq, w_scale, bias)               # bf16 [M, K] -> bf16 [M, N]
+    y = linear_noalloc(x, wq, w_scale, bias, out=y)  # the same, no allocation
                                                    # (fp16 in -> fp16 out)
     xq, a_scale = quant_act(x)                     # the two ops separately
     y = scaled_mm(xq, a_scale, wq, w_scale, bias)
@@ -34,6 +35,7 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 K_MAX = 133144
 K_MAX_PACKED = 132104   # ingest: weights may hold -128
+NOALLOC_SCRATCH_BYTES = 64 << 20
 SMALL_M = 16          # small-M path for K <= 8192
 SMALL_M_WIDE = 32     # ... and up to this M for K <= 4096
 LDO_MAX = 1 << 22
@@ -48,6 +50,7 @@ SYMBOLS = (
     "w8a8_quant_act",
     "w8a8_scaled_mm",
     "w8a8_linear",
+    "w8a8_linear_noalloc",
     "w8a8_quantize_weights_f16",
     "w8a8_quant_act_f16",
     "w8a8_scaled_mm_f16",
@@ -92,6 +95,7 @@ def lib() -> ctypes.CDLL:
     L.w8a8_quant_act.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     L.w8a8_scaled_mm.argtypes = [vp, vp, i64, i64, vp, vp, i64, vp, vp, i64, vp, vp]
     L.w8a8_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp, sz, vp, vp]
+    L.w8a8_linear_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, i64, vp, vp, i64, vp, vp]
     L.w8a8_quantize_weights_f16.argtypes = L.w8a8_quantize_weights.argtypes
     L.w8a8_quant_act_f16.argtypes = L.w8a8_quant_act.argtypes
     L.w8a8_scaled_mm_f16.argtypes = L.w8a8_scaled_mm.argtypes
@@ -110,6 +114,7 @@ def lib() -> ctypes.CDLL:
     L.w8a8_status_string.restype = ctypes.c_char_p
     L.w8a8_last_hip_error.argtypes = []
     for name in ("w8a8_quantize_weights", "w8a8_quant_act", "w8a8_scaled_mm", "w8a8_linear",
+                 "w8a8_linear_noalloc",
                  "w8a8_quantize_weights_f16", "w8a8_quant_act_f16", "w8a8_scaled_mm_f16",
                  "w8a8_linear_f16",
                  "w8a8_linear_path", "w8a8_gemm_tile", "w8a8_unpack_pack_quantized", "w8a16_linear",
@@ -323,6 +328,34 @@ def linear(x, wq, w_scale, bias=None, out=None, workspace=None, acc_debug=None):
     _check(fn, getattr(lib(), fn)(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
                                   _ptr(out), ldo, _ptr(workspace), workspace.numel(),
                                   _ptr(acc_debug), _stream(x.device)))
+    return out
+
+
+def linear_noalloc(x, wq, w_scale, bias=None, out=None, acc_debug=None):
+    """W8A8 linear (bf16 x [M, K] -> bf16 [M, N]) through
+    w8a8_linear_noalloc: the library's per-GPU scratch array replaces the
+    workspace, so the call allocates nothing when `out` is given (for callers
+    that cannot allocate). Calls that overlap on one GPU share that scratch
+    and must be serialised by the caller."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("linear_noalloc takes bf16 activations")
+    M, K, ldx = _rows(x, x.dtype, "x")
+    N, K2, ldw = _rows(wq, torch.int8, "wq")
+    if K2 != K or (N > 1 and ldw != K):
+        raise ValueError("wq must be contiguous [N, K] with the K of x")
+    _vec(w_scale, torch.float32, N, "w_scale")
+    _vec(bias, x.dtype, N, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    Mo, No, ldo = _rows(out, x.dtype, "out")
+    if (Mo, No) != (M, N):
+        raise ValueError("out must be [M, N]")
+    if acc_debug is not None and (acc_debug.shape != (M, N) or acc_debug.dtype != torch.int32
+                                  or not acc_debug.is_contiguous()):
+        raise ValueError("acc_debug must be a contiguous int32 [M, N] tensor")
+    _check("w8a8_linear_noalloc",
+           lib().w8a8_linear_noalloc(_ptr(x), M, K, ldx, _ptr(wq), _ptr(w_scale), N, _ptr(bias),
+                                     _ptr(out), ldo, _ptr(acc_debug), _stream(x.device)))
     return out
 
 

@@ -3,6 +3,8 @@
 // and nothing is kept between calls.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/w8a8.h"
 #include "producers.h"
 #include "w8a8_kernels.h"
@@ -142,6 +144,37 @@ int producer_common(const w8a8::ProducerArgs& p, void* stream) {
 
 }  // namespace
 
+// Scratch of w8a8_linear_noalloc (the workspace w8a8_linear takes from its
+// caller: xq, a_scale and any split-K partial sums). A file-scope device
+// array: each GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not a device
+// address; its address on a device comes from hipGetSymbolAddress.
+__device__ __align__(256) unsigned char scratch[W8A8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};   // address of `scratch` on each device
+
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device (with the device current) and kept.
+int scratch_address(void** ptr) {
+  int dev = 0;
+  if (int s = hip_status(hipGetDevice(&dev))) return s;
+  if (dev < 0 || dev >= kMaxDevices) return W8A8_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int s = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))) return s;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return W8A8_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int w8a8_quantize_weights(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int8_t* wq,
@@ -206,6 +239,22 @@ int w8a8_linear(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8
                 void* stream) {
   return linear_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, workspace, workspace_bytes,
                        acc_debug, stream, false);
+}
+
+int w8a8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
+                        const float* w_scale, int64_t N, const uint16_t* bias, uint16_t* out,
+                        int64_t ldo, int32_t* acc_debug, void* stream) {
+  // every argument check comes before the first HIP call
+  if (int s = check_gemm(M, K, N, wq, w_scale, bias, out, ldo, acc_debug)) return s;
+  if (int s = check_bf16_ld(ldx, K)) return s;
+  if (M == 0) return W8A8_OK;
+  if (!x) return W8A8_ERR_INVALID_ARG;
+  if (!aligned(x, 16)) return W8A8_ERR_MISALIGNED;
+  if (w8a8_linear_workspace_bytes(M, K, N) > W8A8_NOALLOC_SCRATCH_BYTES) return W8A8_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (int s = scratch_address(&ws)) return s;
+  return linear_common(x, M, K, ldx, wq, w_scale, N, bias, out, ldo, ws,
+                       W8A8_NOALLOC_SCRATCH_BYTES, acc_debug, stream, false);
 }
 
 int w8a8_linear_f16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const int8_t* wq,
