@@ -92,8 +92,8 @@ def test_quant_edge_rows():
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 64), (5, 1040, 1040), (7, 16400, 16400),
                                     (2, 20000, 20008), (129, 3072, 3080),
                                     # one 256-thread workgroup per row, 4 and 16 chunks per
-                                    # thread (rows of 4104-8192 and 24584-32768 elements)
-                                    (3, 4104, 4112), (5, 8192, 8192), (2, 24584, 24600),
+                                    # thread (rows of 4112-8192 and 24592-32768 elements)
+                                    (3, 4112, 4120), (5, 8192, 8192), (2, 24592, 24600),
                                     (3, 32768, 32768)])
 def test_quant_ragged_and_strided(M, K, ld):
     rng = np.random.default_rng(M * 7 + K)
@@ -156,7 +156,7 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None, check_ws=True):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (4, 100, 8192), (16, 70, 8192),
                                    (2, 129, 8208), (17, 33, 64), (33, 67, 80),
-                                   (40, 72, 4104), (20, 40, 8192), (3, 40, 24592),
+                                   (40, 72, 4112), (20, 40, 8192), (3, 40, 24592),
                                    (2, 24, 32768),
                                    (67, 17, 208), (16, 300, 112), (65, 129, 1040),
                                    (130, 260, 528), (257, 513, 256), (300, 700, 1296),
