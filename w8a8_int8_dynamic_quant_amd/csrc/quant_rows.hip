@@ -31,19 +31,6 @@ __device__ __forceinline__ void store8(uint2 q, __amdgpu_buffer_rsrc_t r, uint32
   __builtin_amdgcn_raw_buffer_store_b64((v2u){q.x, q.y}, r, off, 0, 0);
 }
 
-// Unsigned max over the 64 lanes of the wave (DPP within rows of 16, then
-// row broadcasts), returned as a wave-uniform value.
-__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false)); // row_ror 4
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false)); // row_ror 8
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast 15
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false)); // row_bcast 31
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-
 template <int CHT, bool F16>
 __global__ __launch_bounds__(256) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
@@ -60,7 +47,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   uint32_t amax = 0;
 #pragma unroll
   for (int u = 0; u < CHT; ++u) amax = absmax_bits8(v[u], amax);
-  amax = wave_max_dpp(amax);
+  amax = wave_max_u32(amax);
   if ((tid & 63) == 0) wmax[wave] = amax;
   lds_barrier();
   amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
@@ -106,7 +93,7 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(
   uint32_t amax = 0;
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) amax = absmax_bits8(v[c], amax);
-  amax = wave_max_dpp(amax);
+  amax = wave_max_u32(amax);
   if constexpr (P == 2) {
     if (lane == 0) part_max[wave] = amax;
     lds_barrier();
@@ -148,7 +135,7 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) amax = absmax_bits8(v[u], amax);
   }
-  amax = wave_max_dpp(amax);
+  amax = wave_max_u32(amax);
   const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;

@@ -13,11 +13,14 @@
 //  1. the M activation rows are quantised on chip (per-row amax, scale =
 //     amax/127, exact half-to-even rounding) into LDS as int8 [M][K];
 //     workgroup 0 also writes xq and a_scale out for the caller. The rows
-//     are requested before any weight window (vector-memory requests of the
-//     whole chip share the same queues, and the few KiB of x requested behind
-//     the weight stream would arrive last); the windows follow at once. With M <= W (at most one
-//     row per wave) the quantisation itself then runs while the weights
-//     stream;
+//     are requested before any weight window (a wave's loads complete in
+//     order, so rows requested behind its windows would arrive last). With
+//     at most two rows per wave (M <= 2W), the first kD0 windows follow the
+//     row loads at once, the wave quantises its rows as soon as they land,
+//     and only then requests its remaining windows: a wave that requests
+//     every window first stalls at issue once the CU's request queue is full,
+//     and its rows wait behind the stall (measured at M = 16 on 3072 ->
+//     18432: 16.1 us with every window first, 15.0 us with kD0 = 8);
 //  2. the wave requests up to kD 128-byte windows of its rows at once
 //     (one buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte
 //     chunk l/8, so every instruction fetches 8 whole 128-byte lines).
@@ -42,6 +45,7 @@ namespace w8a8 {
 namespace {
 
 constexpr int kD = 24;                   // 128-byte windows in flight per wave
+constexpr int kD0 = 8;                   // of these, requested before the rows are quantised
 constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisation batch
 constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
 
@@ -131,6 +135,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     float* __restrict__ sa_out, int vec_flags, int G) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ float sa_lds[8 * TB];
+  // TWO_ROWS: the epilogue scales and biases of each wave's rows, parked
+  // here once they have landed (in registers across the stream they would
+  // make this mode spill)
+  __shared__ float scl_lds[MODE == TWO_ROWS ? kMaxWaves : 1][16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -143,6 +151,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   const int64_t n_base = ((int64_t)blockIdx.x * G + wave) * 8;
   const int rows_valid = wave < G ? (int)max<int64_t>(0, min<int64_t>(8, N - n_base)) : 0;
   const uint32_t nchunks = (uint32_t)(K >> 3);
+  // epilogue scale and bias (row n_base + lane % 8), requested before anything else
+  float sw1, bb1;
+  load_row_scale<HAS_BIAS, F16>(a.w_scale, a.bias, n_base, rows_valid, lane, sw1, bb1);
   const bool write_q = blockIdx.x == 0;
 
   // weight windows: lane l reads row l%8, 16-byte chunk l/8 of window w
@@ -185,11 +196,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int u = 0; u < kQ; ++u) v2[u] = load16(rx2, (uint32_t)(lane + 64 * u) * 16u);
     }
-    // the weight requests go out right behind the row loads; vmcnt(kD) then
-    // waits for the rows only (loads complete in order)
+    // the first kD0 weight requests go out right behind the row loads;
+    // vmcnt(kD0) then waits for the rows only (loads complete in order)
     __builtin_amdgcn_sched_barrier(0);
-    issue_all();
-    wait_vmcnt<kD>();
+#pragma unroll
+    for (int d = 0; d < kD0; ++d) buf[d] = wload(d);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kD0>();
+    if constexpr (R2) {
+      if (lane < 8) {
+        scl_lds[wave][lane] = sw1;
+        scl_lds[wave][8 + lane] = bb1;
+      }
+    }
     if (wave < M) {
       const float s = quantise_regs<F16>(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
                                     write_q);
@@ -208,6 +227,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
         }
       }
     }
+    // the remaining windows, once the rows are in LDS
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = kD0; d < kD; ++d) buf[d] = wload(d);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
   } else {
     for (int m = wave; m < M; m += W) {
@@ -277,16 +301,20 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   for (int t = 0; t < TB; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[t][r] = acc[t][r] + __builtin_amdgcn_ds_bpermute(src, acc[t][r]);
+  float sw[4], bb[4];
+  if constexpr (MODE == TWO_ROWS) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sw[r] = scl_lds[wave][4 * ((lane >> 4) & 1) + r];
+      bb[r] = scl_lds[wave][8 + 4 * ((lane >> 4) & 1) + r];
+    }
+  } else {
+    gather4(sw1, 4 * ((lane >> 4) & 1), sw);
+    gather4(bb1, 4 * ((lane >> 4) & 1), bb);
+  }
   if ((lane & 8) != 0 || lane >= 32) return;
   const int nl = 4 * (lane >> 4);
   const int64_t n = n_base + nl;
-  float sw[4], bb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const bool ok = nl + r < rows_valid;
-    sw[r] = ok ? a.w_scale[n + r] : 0.f;
-    bb[r] = (HAS_BIAS && ok) ? half_to_f32<F16>(a.bias[n + r]) : 0.f;
-  }
 #pragma unroll
   for (int blk = 0; blk < TB; ++blk) {
     const int m = 8 * blk + (lane & 7);

@@ -94,6 +94,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
   const int nwin = (int)((K + 127) / 128);
   const int64_t n_base = ((int64_t)blockIdx.x * W + wave) * 8;
   const int rows_valid = (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
+  // epilogue scale and bias (row n_base + lane % 8), requested before anything else
+  float sw1, bb1;
+  load_row_scale<HAS_BIAS, F16>(a.w_scale, a.bias, n_base, rows_valid, lane, sw1, bb1);
 
   // ---- 1. activation rows into LDS (LDS-DMA: lane l of an instruction
   // writes the 16 bytes at LDS base + 16*l) ----
@@ -191,16 +194,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void w8a16_kernel(const uint16_t* _
     s0[r] = c0 + __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(c0)));
     s1[r] = TWO ? c1 + __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(c1))) : 0.f;
   }
+  float sw[4], bb[4];
+  gather4(sw1, 4 * ((lane >> 4) & 1), sw);
+  gather4(bb1, 4 * ((lane >> 4) & 1), bb);
   if ((lane & 8) != 0 || lane >= 32) return;
   const int nl = 4 * (lane >> 4);
   const int64_t n = n_base + nl;
-  float sw[4], bb[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const bool ok = nl + r < rows_valid;
-    sw[r] = ok ? a.w_scale[n + r] : 0.f;
-    bb[r] = (HAS_BIAS && ok) ? half_to_f32<F16>(a.bias[n + r]) : 0.f;
-  }
 #pragma unroll
   for (int blk = 0; blk < (TWO ? 2 : 1); ++blk) {
     const int m = 8 * blk + (lane & 7);

@@ -103,30 +103,29 @@ __device__ __forceinline__ float row_scale(uint32_t amax_bits16) {
 }
 
 // Quantisation of one value: round(fl32(x / s)) half to even, clamped to
-// [-127, 127], computed as rint(t) with t = fl32(x * r), r = fl32(1 / s),
-// for a normal s.
+// [-127, 127], computed as rint(P) for the exact product P = x * r, with
+// r = fl32(1 / s) for a normal s. P is never rounded on its own: it enters
+// one fma, m = fl32(P + 1.5 * 2^23).
 //
-// t differs from the exact quotient Q = x/s by at most |Q|(2u + u^2) and
-// fl32(Q) differs from Q by at most |Q|u (u = 2^-24). |Q| <= amax/s <=
-// 127 / (1 - u), so |t - fl32(Q)| < 2.3e-5 < 2^-15. If t is farther than
-// 2^-15 from every half-integer, no rounding boundary lies between t and
-// fl32(Q) and rint(t) == rint(fl32(Q)). Otherwise (`near` is set) the caller
-// redoes the element with the IEEE division. (t - rint(t) is exact by
-// Sterbenz's lemma, so the distance test itself does not round.) The same
-// bound gives |t| < 127 (1 + 3u) < 127.5, so rint(t) needs no clamp.
-//
-// The rounding is the fp32 addition m = fl32(t + 1.5 * 2^23): every value
-// in [2^23, 2^24) is an integer, so m = 1.5 * 2^23 + rint(t) (round to
-// nearest even), rint(t) = m - 1.5 * 2^23 exactly, and the low byte of m's
-// bit pattern is rint(t) as a two's-complement int8. Returns m's bits.
+// r = (1/s)(1 + d) with |d| <= u (u = 2^-24), so P differs from the exact
+// quotient Q = x/s by at most |Q|u, and fl32(Q) differs from Q by at most
+// |Q|u. |Q| <= amax/s <= 127 / (1 - u), so |P - fl32(Q)| < 254.01u < 2^-16.
+// Every value in [2^23, 2^24) is an integer, so m = 1.5 * 2^23 + rint(P)
+// (round to nearest even), rint(P) = m - 1.5 * 2^23 exactly, and the low
+// byte of m's bit pattern is rint(P) as a two's-complement int8 (|P| <
+// 127.5, so no clamp). The distance e = fl32(P - rint(P)) is a second fma
+// (|P - rint(P)| <= 1/2, so it rounds by at most 2^-26). If |e| <
+// 1/2 - 2^-15, then |fl32(Q) - rint(P)| < 1/2 - 2^-15 + 2^-26 + 2^-16 <
+// 1/2 and rint(fl32(Q)) == rint(P). Otherwise the value lies near a
+// rounding boundary and the caller redoes it with the IEEE division.
+// Returns m's bits; dist receives |e|.
 constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr float kNearHalf = 0.5f - 0x1p-15f;
 
-__device__ __forceinline__ uint32_t quant_mul(float x, float r, bool& near) {
-  const float t = x * r;
-  const float m = t + kRoundMagic;
-  const float rt = m - kRoundMagic;
-  // |t - rint(t)| <= 1/2, so "within 2^-15 of a half-integer" is one compare
-  near = __builtin_fabsf(t - rt) >= 0.5f - 0x1p-15f;
+__device__ __forceinline__ uint32_t quant_fma(float x, float r, float& dist) {
+  const float m = __builtin_fmaf(x, r, kRoundMagic);
+  // kRoundMagic - m is -rint(P), exactly
+  dist = __builtin_fabsf(__builtin_fmaf(x, r, kRoundMagic - m));
   return __float_as_uint(m);
 }
 
@@ -160,24 +159,25 @@ __device__ __forceinline__ uint2 quant8(uint4 v, float s, float r, bool zero, bo
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   float x[8];
   uint32_t q[8];
-  bool any_near = false;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = half_to_f32<F16>(w[i] & 0xffffu);
     x[2 * i + 1] = half_to_f32<F16>(w[i] >> 16);
   }
+  // the largest distance of the eight decides whether any is near
+  float dmax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    bool near;
-    q[i] = quant_mul(x[i], r, near);
-    any_near |= near;
+    float d;
+    q[i] = quant_fma(x[i], r, d);
+    dmax = __builtin_fmaxf(dmax, d);
   }
-  if (__builtin_amdgcn_ballot_w64(any_near || exact_div)) {
+  if (__builtin_amdgcn_ballot_w64(dmax >= kNearHalf || exact_div)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      bool near;
-      quant_mul(x[i], r, near);
-      if (near || exact_div) q[i] = quant_div(x[i], s);
+      float d;
+      quant_fma(x[i], r, d);
+      if (d >= kNearHalf || exact_div) q[i] = quant_div(x[i], s);
     }
   }
   return make_uint2(pack_low_bytes4(q[0], q[1], q[2], q[3]), pack_low_bytes4(q[4], q[5], q[6], q[7]));
@@ -193,10 +193,46 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v, uint32_t m) {
   return m;
 }
 
+// Unsigned max over the 64 lanes of the wave (DPP within rows of 16, then
+// row broadcasts), returned as a wave-uniform value. Every lane must be
+// active.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x124, 0xF, 0xF, false)); // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x128, 0xF, 0xF, false)); // row_ror 8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false)); // row_bcast 15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false)); // row_bcast 31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The weight scale and bias (converted to fp32) of output row
+// n_base + (lane & 7) of a small-M wave, read through descriptors bounded at
+// the wave's rows_valid rows (zero past them). The small-M kernels request
+// these first: requested after the weight stream, they would be served last
+// and hold the epilogue back. One pair per lane keeps two registers live
+// across the stream; gather4 hands each epilogue lane the four it needs.
+template <bool HAS_BIAS, bool F16>
+__device__ __forceinline__ void load_row_scale(const float* w_scale, const uint16_t* bias,
+                                               int64_t n_base, int rows_valid, int lane,
+                                               float& sw, float& bb) {
+  const uint32_t nv = rows_valid > 0 ? (uint32_t)rows_valid : 0u;
+  const int64_t nb = rows_valid > 0 ? n_base : 0;
+  const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(w_scale + nb, nv * 4u);
+  sw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sw, (lane & 7) * 4, 0, 0));
+  bb = 0.f;
+  if constexpr (HAS_BIAS) {
+    const __amdgpu_buffer_rsrc_t r_b = make_rsrc(bias + nb, nv * 2u);
+    bb = half_to_f32<F16>(__builtin_amdgcn_raw_buffer_load_b16(r_b, (lane & 7) * 2, 0, 0));
+  }
+}
+
+// out[r] = v of lane first + r (r = 0..3); every lane of the wave must be
+// active.
+__device__ __forceinline__ void gather4(float v, int first, float (&out)[4]) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
+  for (int r = 0; r < 4; ++r)
+    out[r] = __int_as_float(__builtin_amdgcn_ds_bpermute((first + r) * 4, __float_as_int(v)));
 }
 
 // Scale epilogue for one element (fixed order, no contraction). Without a
