@@ -328,6 +328,36 @@ def test_linear_256_tile_store_paths(N, with_bias):
     print(_linear_case(x, w, b)[0])
 
 
+def _pp_halves(M, N):
+    """True when the 256x256 kernel runs the last round of some XCD's tiles
+    as 128-row halves (the rule the launcher applies: per XCD of cus/8
+    compute units, tiles beyond whole rounds, when at most half a round)."""
+    cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
+    T = -(-M // 256) * -(-N // 256)
+    for x in range(8):
+        tx = T // 8 + (1 if x < T % 8 else 0)
+        rem = tx % cpx if tx > cpx else 0
+        if 0 < rem and 2 * rem <= cpx:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("M,N,K,with_bias", [(4152, 9224, 272, True), (4100, 9218, 272, False),
+                                             (4352, 9220, 1040, True), (4352, 12288, 208, False)])
+def test_linear_256_tile_halves(M, N, K, with_bias):
+    """Tiles of the last round split into 128-row halves: a last M tile whose
+    second half is empty (4100: 4 rows in the first) or ragged (4152), the
+    three store paths (N % 8 == 0, N % 4 == 0, else) and a K tail."""
+    assert w8.gemm_tile(M, K, N) == (256, 256)
+    assert _pp_halves(M, N)
+    rng = np.random.default_rng(M + N + K)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    b = random_bf16(rng, (N,), 0.01) if with_bias else None
+    announce(f"256 tile halves M={M} N={N} K={K} bias={with_bias}")
+    print(_linear_case(x, w, b)[0])
+
+
 # Split K: shapes whose 256x256 tiles fill at most half of the compute units
 # or whose 128x128 tiles fill at most one round (K split in two), and skinny
 # shapes on 64x64 tiles (K split in up to four); w8a8_linear then splits K

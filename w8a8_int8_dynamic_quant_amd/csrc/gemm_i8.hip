@@ -96,6 +96,41 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = r / gm;
 }
 
+// Block -> tile for the ping-pong kernel. XCD x (blockIdx & 7; the hardware
+// hands workgroups to the XCDs in turn) takes the same contiguous run of
+// tiles as tile_coords, in dispatch order. When cpx > 0 and the last round
+// of that run over the XCD's cpx compute units is at most half full, its
+// last tiles are split into two 128-row halves (half = 0, 1), numbered after
+// the whole tiles (half = -1), so the last round runs twice as many pieces
+// of half the work. Returns false for a block past its XCD's pieces.
+__device__ __forceinline__ bool tile_coords_halves(int tiles_m, int tiles_n, int cpx, int& tm,
+                                                   int& tn, int& half) {
+  const int T = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, local = b >> 3;
+  const int tx = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
+  const int rem = (cpx > 0 && tx > cpx) ? tx % cpx : 0;
+  const int whole = (rem > 0 && 2 * rem <= cpx) ? tx - rem : tx;
+  int t = xcd * (T >> 3) + min(xcd, T & 7);
+  half = -1;
+  if (local < whole) {
+    t += local;
+  } else {
+    const int h = local - whole;
+    if (h >= 2 * (tx - whole)) return false;
+    t += whole + (h >> 1);
+    half = h & 1;
+  }
+  constexpr int G = 4;     // m-tiles per group, as tile_coords
+  const int group = t / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int r = t - group * G * tiles_n;
+  tm = first_m + r % gm;
+  tn = r / gm;
+  return true;
+}
+
 // Instruction order of one stage for the scheduler: the fragment reads of
 // k-step 0, then per k-step its MFMAs in groups, each group followed by one
 // fragment read of the next k-step and (in the first half of the stage) by
@@ -450,18 +485,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_i8_kernel(GemmArg
   }
 }
 
-// Epilogue of the eight-wave kernels: the wave's 128 x 64 sub-tile (rows
-// 128 grp.., columns 64 wn.. of the tile), scaled in the fp32 order of the
+// Epilogue of the eight-wave kernels: the wave's 32 FM x 64 sub-tile (rows
+// 32 FM grp.., columns 64 wn.. of the tile), scaled in the fp32 order of the
 // oracle and stored as bf16 (fp16). With 16-byte output rows it is staged in
 // the wave's own 16 KiB of LDS (`region`) and written as whole 128-byte row
 // segments; no other wave touches the region, so no barrier is needed.
-template <bool HAS_BIAS, bool F16, int HALVES = 1>
-__device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (&acc)[2][4],
+template <bool HAS_BIAS, bool F16, int HALVES = 1, int FM = 4>
+__device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (&acc)[2][FM],
                                                  const float* lds_sa, const float* lds_sw,
                                                  const float* lds_b, int8_t* region, int64_t m0,
                                                  int64_t n0, uint32_t rows_x, uint32_t rows_w,
                                                  int grp, int wn, int lane, int vec_flags) {
-  constexpr int FN = 2, FM = 4;
+  constexpr int FN = 2;
   const int frag_row = lane & 31, frag_half = lane >> 5;
   const int64_t N = a.N;
   const int64_t ldo = a.ldo;
@@ -469,7 +504,7 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
       make_rsrc(a.out + m0 * ldo + n0, (uint32_t)(((int64_t)(rows_x - 1) * ldo + rows_w) * 2));
   float sa[FM];
 #pragma unroll
-  for (int j = 0; j < FM; ++j) sa[j] = lds_sa[128 * grp + 32 * j + frag_row];
+  for (int j = 0; j < FM; ++j) sa[j] = lds_sa[32 * FM * grp + 32 * j + frag_row];
   // visit(nl, ml, y01, y23): four outputs at wave-local column nl, row ml,
   // for the row blocks jb .. jb+jn-1
   auto for_each_out = [&](auto&& visit, int jb = 0, int jn = FM) {
@@ -497,9 +532,9 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
       }
     }
   };
-  const int row_base = 128 * grp, col_base = 64 * wn;
+  const int row_base = 32 * FM * grp, col_base = 64 * wn;
   if (vec_flags & 4) {
-    // HALVES passes over 128 / HALVES rows each: rows of 128 bytes in the
+    // HALVES passes over 32 FM / HALVES rows each: rows of 128 bytes in the
     // region, 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7)
     constexpr int JN = FM / HALVES, ROWS = 32 * JN;
     const int c = lane & 7;
@@ -578,28 +613,25 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
 // capacity, only waves that are not issuing MFMAs wait on it, and a request
 // has about five phases to land. Group 0's epilogue runs alongside group
 // 1's last MFMAs.
-template <bool HAS_BIAS, bool F16, bool SPLIT>
-__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
-                                                        int vec_flags, int kps) {
-  constexpr int BM = 256, BN = 256, BK = 64, KS = BK / 32;
-  constexpr int FN = 2, FM = 4;
+//
+// A tile is whole (FM = 4: 256 x 256) or, in the last round of an XCD's
+// tiles, one of two 128-row halves (FM = 2: 128 x 256, each wave a 64 x 64
+// sub-tile, eight MFMAs per stage). A half runs the same loop: group 1's
+// requests for rows 128.. of the xq panel read out of bounds (no memory
+// traffic, zeros into LDS rows nothing reads), so every wait keeps its
+// constant.
+template <bool HAS_BIAS, bool F16, bool SPLIT, int FM>
+__device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n0, int vec_flags,
+                                        int kps, int8_t* lds0, int8_t* lds1, int8_t* lds2,
+                                        int8_t* lds3, float* lds_sa, float* lds_sw, float* lds_b) {
+  constexpr int BM = 64 * FM, BN = 256, BK = 64, KS = BK / 32;
+  constexpr int FN = 2;
   constexpr int HALF = 256 * BK;             // one panel of a stage: 16 KiB
   constexpr int LPW = 4;                     // requests per wave per stage (its group's panel)
-
-  __shared__ __attribute__((aligned(1024))) int8_t lds0[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds1[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds2[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds3[2 * HALF];
-  __shared__ __attribute__((aligned(16))) float lds_sa[BM];
-  __shared__ __attribute__((aligned(16))) float lds_sw[BN];
-  __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2, wn = wave & 3;
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t M = a.M, N = a.N, K = a.K;
 
   const uint32_t rows_w = (uint32_t)min<int64_t>(BN, N - n0);
@@ -609,11 +641,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, i
   {
     const __amdgpu_buffer_rsrc_t r_sa = make_rsrc(a.a_scale + m0, rows_x * 4u);
     const __amdgpu_buffer_rsrc_t r_sw = make_rsrc(a.w_scale + n0, rows_w * 4u);
-    if (tid < BM)
+    // threads 0..255 the row scales (zero past the tile's rows), 256.. the
+    // column scales
+    if (tid < 256)
       lds_sa[tid] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sa, tid * 4, 0, 0));
     else
-      lds_sw[tid - BM] =
-          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sw, (tid - BM) * 4, 0, 0));
+      lds_sw[tid - 256] =
+          __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sw, (tid - 256) * 4, 0, 0));
     if constexpr (HAS_BIAS) {
       const __amdgpu_buffer_rsrc_t r_b = make_rsrc(a.bias + n0, rows_w * 2u);
       if (tid < BN) lds_b[tid] = half_to_f32<F16>(__builtin_amdgcn_raw_buffer_load_b16(r_b, tid * 2, 0, 0));
@@ -650,7 +684,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, i
   // the swizzle c ^ ((row >> 2) & 3), i.e. fb ^ (32 ks)
   const int frag_row = lane & 31, frag_half = lane >> 5;
   const int fb = frag_row * BK + 16 * (frag_half ^ ((frag_row >> 2) & 3));
-  const int w_row0 = 64 * wn * BK, x_row0 = HALF + 128 * grp * BK;
+  const int w_row0 = 64 * wn * BK, x_row0 = HALF + 32 * FM * grp * BK;
 
   v4i fw[KS][FN], fx[KS][FM];
   auto read_frags = [&](const int8_t* st) {
@@ -737,7 +771,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, i
     for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        const int ml = 128 * grp + 32 * j + frag_row;
+        const int ml = 32 * FM * grp + 32 * j + frag_row;
         const v16i& c = acc[i][j];
         const v4i run[4] = {c.lo.lo, c.lo.hi, c.hi.lo, c.hi.hi};
 #pragma unroll
@@ -759,8 +793,34 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, i
   const int n_st = ke - kb;
   const int pick = grp == 0 ? ((n_st - 1) & 3) : (n_st & 3);
   int8_t* const stage_buf = pick == 0 ? lds0 : pick == 1 ? lds1 : pick == 2 ? lds2 : lds3;
-  gemm_pp_epilogue<HAS_BIAS, F16, 2>(a, acc, lds_sa, lds_sw, lds_b, stage_buf + wn * 8192, m0, n0,
-                                     rows_x, rows_w, grp, wn, lane, vec_flags);
+  gemm_pp_epilogue<HAS_BIAS, F16, 2, FM>(a, acc, lds_sa, lds_sw, lds_b, stage_buf + wn * 8192, m0,
+                                         n0, rows_x, rows_w, grp, wn, lane, vec_flags);
+}
+
+// cpx: compute units per XCD when the last round of each XCD's tiles may be
+// split into halves (0: never).
+template <bool HAS_BIAS, bool F16, bool SPLIT>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
+                                                        int vec_flags, int kps, int cpx) {
+  constexpr int HALF = 256 * 64;
+  __shared__ __attribute__((aligned(1024))) int8_t lds0[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds1[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds2[2 * HALF];
+  __shared__ __attribute__((aligned(1024))) int8_t lds3[2 * HALF];
+  __shared__ __attribute__((aligned(16))) float lds_sa[256];
+  __shared__ __attribute__((aligned(16))) float lds_sw[256];
+  __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? 256 : 1];
+  int tm, tn, half;
+  if (!tile_coords_halves(tiles_m, tiles_n, cpx, tm, tn, half)) return;
+  if (half < 0) {
+    pp_tile<HAS_BIAS, F16, SPLIT, 4>(a, (int64_t)tm * 256, (int64_t)tn * 256, vec_flags, kps, lds0,
+                                     lds1, lds2, lds3, lds_sa, lds_sw, lds_b);
+  } else if constexpr (!SPLIT) {
+    const int64_t m0 = (int64_t)tm * 256 + 128 * half;
+    if (m0 < a.M)
+      pp_tile<HAS_BIAS, F16, SPLIT, 2>(a, m0, (int64_t)tn * 256, vec_flags, kps, lds0, lds1, lds2,
+                                       lds3, lds_sa, lds_sw, lds_b);
+  }
 }
 
 // Split K, second step: out[m, n..n+7] = epilogue(sum over the slices of
@@ -829,22 +889,42 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
   return hipGetLastError();
 }
 
+// Blocks of the ping-pong kernel for T tiles with the last round of each
+// XCD's run split into halves where tile_coords_halves does so (cpx compute
+// units per XCD): 8 times the largest number of pieces of one XCD.
+int64_t pp_blocks(int64_t T, int cpx) {
+  int64_t most = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int64_t tx = (T >> 3) + (x < (T & 7) ? 1 : 0);
+    const int64_t rem = (cpx > 0 && tx > cpx) ? tx % cpx : 0;
+    const int64_t whole = (rem > 0 && 2 * rem <= cpx) ? tx - rem : tx;
+    most = std::max(most, whole + 2 * (tx - whole));
+  }
+  return 8 * most;
+}
+
 // 256 x 256 tiles: the eight-wave ping-pong kernel (kps counts 128-byte
-// stages, as the split-K plan does).
+// stages, as the split-K plan does). Without split K, the last round of
+// each XCD's tiles runs as 128-row halves when it is at most half full
+// (4352 x 3072 x 9216, 612 tiles: 76 or 77 per XCD of 32 compute units,
+// so 12 or 13 tiles in the last round become 24 or 26 halves).
 hipError_t launch_pp(const GemmArgs& a, hipStream_t stream, int splits = 1, int kps = 0) {
   constexpr int T = 256, BK = 64;
   const int64_t tiles_m = (a.M + T - 1) / T, tiles_n = (a.N + T - 1) / T;
   const int vec_flags = epilogue_vec_flags(a);
   kps = splits == 1 ? (int)((a.K + BK - 1) / BK) : 2 * kps;
-  const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
   if (splits > 1) {
+    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
     hipLaunchKernelGGL((gemm_pp_kernel<false, false, true>), grid, block, 0, stream, a,
-                       (int)tiles_m, (int)tiles_n, vec_flags, kps);
+                       (int)tiles_m, (int)tiles_n, vec_flags, kps, 0);
     return hipGetLastError();
   }
+  const int cus = device_cus();
+  const int cpx = cus % 8 == 0 ? cus / 8 : 0;
+  const dim3 grid((unsigned)pp_blocks(tiles_m * tiles_n, cpx)), block(512);
 #define W8A8_PP(B, H)                                                                           \
   hipLaunchKernelGGL((gemm_pp_kernel<B, H, false>), grid, block, 0, stream, a, (int)tiles_m, \
-                     (int)tiles_n, vec_flags, kps)
+                     (int)tiles_n, vec_flags, kps, cpx)
   if (a.f16) {
     if (a.bias) W8A8_PP(true, true);
     else W8A8_PP(false, true);
