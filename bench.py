@@ -38,7 +38,7 @@ METRIC = ("int8 TOPS + % of MI355X int8 MFMA peak (HBM GB/s for M≤16), per sha
 PEAK_INT8_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 GEMM_KERNEL = "gemm_pp_kernel"          # the 256x256-tile kernel all four DiT shapes take
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_i8_dit_block_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gemm_pp_dit_block_counters.json")
 
 
 class HipEvents:
@@ -94,6 +94,10 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), the "
                         "reference for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE to bytes")
+    p.add_argument("--profile-linear", default="", metavar="M,K,N",
+                   help="only run w8a8_linear (bias, bf16) on one shape, --steps calls after "
+                        "--warmup, weights rotated over copies of 512 MB or more; for "
+                        "rocprofv3 runs of a single shape")
     return p.parse_args()
 
 
@@ -107,6 +111,32 @@ def copy_calibration(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def profile_linear(shape: str, steps: int, warmup: int) -> None:
+    import torch
+
+    import w8a8_int8_dynamic_quant_amd as w8
+    M, K, N = (int(v) for v in shape.split(","))
+    copies = max(2, -(-(512 << 20) // (N * K)))
+    g = torch.Generator(device="cpu").manual_seed(11)
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16).cuda()
+    w = (torch.randn((N, K), generator=g) * 0.02).to(torch.bfloat16).cuda()
+    wq, sw = w8.quantize_weights(w)
+    wqs = [wq.clone() for _ in range(copies)]
+    bias = (torch.randn((N,), generator=g) * 0.01).to(torch.bfloat16).cuda()
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((max(1, w8.workspace_bytes(M, K, N)),), dtype=torch.uint8, device="cuda")
+    for i in range(warmup):
+        w8.linear(x, wqs[i % copies], sw, bias, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w8.linear(x, wqs[i % copies], sw, bias, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / max(1, steps) * 1e6
+    print(json.dumps({"profile_linear": [M, K, N], "path": w8.linear_path(M, K, N),
+                      "calls": steps, "us_per_call_wall": us}), flush=True)
 
 
 # The sources the GEMM kernel is compiled from (its file and the headers it
@@ -486,6 +516,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.profile_linear:
+        profile_linear(args.profile_linear, args.steps, args.warmup)
         return
 
     import numpy as np
