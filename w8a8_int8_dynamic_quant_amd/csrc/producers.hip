@@ -306,16 +306,17 @@ __global__ __launch_bounds__(256) void gelu_table_kernel() {
 
 // WPR waves per row (wave part p holds chunks lane + 64 (p + WPR c), c < CH),
 // 16 / WPR rows per iteration of the workgroup. Each wave requests its part
-// of the row DEPTH iterations ahead before it works on the current one, so
-// DEPTH + 1 rows per wave stay in flight; the parts of a row exchange their
-// amax through LDS slots, double-buffered by iteration so one barrier per
-// iteration suffices (no wave runs more than one iteration ahead of
-// another). Every wave of a workgroup runs the same number of iterations; a
-// row past M reads zero and stores nothing.
-template <int OP, int CH, int WPR, int DEPTH>
+// of the next iteration's row before it works on the current one, into the
+// other of two register buffers (the loop is unrolled by two, so the buffers
+// swap by name: a register copy of a row still in flight would wait for it
+// there); the parts of a row exchange their amax through LDS slots,
+// double-buffered by iteration so one barrier per iteration suffices (no wave
+// runs more than one iteration ahead of another). Every wave of a workgroup
+// runs the same number of iterations; a row past M reads zero and stores
+// nothing.
+template <int OP, int CH, int WPR>
 __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(ProducerArgs a) {
   static_assert(WPR == 4 || WPR == 8 || WPR == 16, "waves per row");
-  static_assert(DEPTH == 1 || DEPTH == 2, "rows requested ahead");
   constexpr int RPI = kLutWaves / WPR;               // rows per iteration
   extern __shared__ __attribute__((aligned(16))) uint16_t lut[];
   __shared__ uint32_t part_max[2][kLutWaves];
@@ -343,32 +344,35 @@ __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(Producer
 #pragma unroll
     for (int c = 0; c < CH; ++c) dst[c] = load16_nt(rx, off0 + kStep * c);
   };
-  int64_t row = (int64_t)blockIdx.x * RPI + wave / WPR;
-  uint4 b[DEPTH + 1][CH];                            // b[0]: this iteration's row
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_row(row + d * stride, b[d]);
-  __syncthreads();                                  // the table is in LDS
-  for (int k = 0; (int64_t)blockIdx.x * RPI + k * stride < a.M; ++k, row += stride) {
-    load_row(row + DEPTH * stride, b[DEPTH]);
-    uint4 (&v)[CH] = b[0];
+  // iteration k on row `row` held in v
+  auto process = [&](int k, int64_t row, uint4 (&v)[CH]) {
     const bool in = row < a.M;
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y + (in ? row : 0) * a.ldy,
-                                                (a.y && in) ? (uint32_t)a.K * 2u : 0u);
-    // the table maps 0 (a chunk past K) to 0
+    // every lookup of the part is requested before the first is used: one
+    // LDS round trip for all of them (the table maps 0, a chunk past K, to 0)
+    // (each pair is loaded into the two halves of one register)
+    typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+    v2u16 y2[CH][4];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y2[c][i].x = lut[w[i] & 0xffffu];
+        y2[c][i].y = lut[w[i] >> 16];
+      }
+    }
     uint32_t amax = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w[i] = (uint32_t)lut[w[i] & 0xffffu] | ((uint32_t)lut[w[i] >> 16] << 16);
-        // the packed pair exists before the y store's branch (else both
-        // halves of every chunk stay live until the quantisation)
-        asm volatile("" : "+v"(w[i]));
-      }
-      v[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      v[c] = make_uint4(__builtin_bit_cast(uint32_t, y2[c][0]), __builtin_bit_cast(uint32_t, y2[c][1]),
+                        __builtin_bit_cast(uint32_t, y2[c][2]), __builtin_bit_cast(uint32_t, y2[c][3]));
       amax = absmax_bits8(v[c], amax);
-      if (a.y) store16(v[c], ry, off0 + kStep * c);
+    }
+    if (a.y) {
+      const __amdgpu_buffer_rsrc_t ry =
+          make_rsrc(a.y + (in ? row : 0) * a.ldy, in ? (uint32_t)a.K * 2u : 0u);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) store16(v[c], ry, off0 + kStep * c);
     }
     amax = wave_max_u32(amax);
     if (lane == 0) part_max[k & 1][wave] = amax;
@@ -387,14 +391,23 @@ __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(Producer
         store8(quant8<false>(v[c], s, r, zero, exact_div), rq, (off0 >> 1) + (kStep >> 1) * c);
       if (lane == 0 && part == 0) a.a_scale[row] = s;
     }
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-#pragma unroll
-      for (int c = 0; c < CH; ++c) b[d][c] = b[d + 1][c];
+  };
+  // iteration k runs while the workgroup's first row of it is below M
+  auto live = [&](int k) { return (int64_t)blockIdx.x * RPI + k * stride < a.M; };
+  int64_t row = (int64_t)blockIdx.x * RPI + wave / WPR;
+  uint4 b0[CH], b1[CH];
+  load_row(row, b0);
+  __syncthreads();                                  // the table is in LDS
+  for (int k = 0; live(k); k += 2, row += 2 * stride) {
+    load_row(row + stride, b1);
+    process(k, row, b0);
+    if (!live(k + 1)) break;
+    load_row(row + 2 * stride, b0);
+    process(k + 1, row + stride, b1);
   }
 }
 
-template <int OP, int CH, int WPR, int DEPTH>
+template <int OP, int CH, int WPR>
 hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((gelu_table_kernel<OP>), dim3(256), dim3(256), 0, stream);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -402,7 +415,7 @@ hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
   const int64_t wgs_needed = (a.M + RPI - 1) / RPI;
   const int64_t cus = device_cus();
   const unsigned grid = (unsigned)(wgs_needed < cus ? wgs_needed : cus);
-  hipLaunchKernelGGL((gelu_lut_quant_kernel<OP, CH, WPR, DEPTH>), dim3(grid), dim3(64 * kLutWaves),
+  hipLaunchKernelGGL((gelu_lut_quant_kernel<OP, CH, WPR>), dim3(grid), dim3(64 * kLutWaves),
                      kLutBytes, stream, a);
   return hipGetLastError();
 }
@@ -415,16 +428,15 @@ constexpr int64_t kLutMaxChunks = 2048;
 
 template <int OP>
 hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
-  // waves per row, rows requested ahead: at 4352 x 12288, 4 and 1 ran in
-  // 45 us, 8 and 1 in 50 us, 16 and 2 in 57 us (wider rows mean more waves
-  // at each barrier; deeper prefetch, more register moves)
-  constexpr int W = 4, D = 1;
+  // waves per row: at 4352 x 12288, 4 ran in 45 us, 8 in 50 us, 16 in
+  // 57 us (wider rows mean more waves at each barrier)
+  constexpr int W = 4;
   const int64_t per_lane = ((a.K >> 3) + 64 * W - 1) / (64 * W);
-  if (per_lane <= 1) return launch_lut<OP, 1, W, D>(a, stream);
-  if (per_lane <= 2) return launch_lut<OP, 2, W, D>(a, stream);
-  if (per_lane <= 4) return launch_lut<OP, 4, W, D>(a, stream);
-  if (per_lane <= 6) return launch_lut<OP, 6, W, D>(a, stream);
-  return launch_lut<OP, 8, W, D>(a, stream);
+  if (per_lane <= 1) return launch_lut<OP, 1, W>(a, stream);
+  if (per_lane <= 2) return launch_lut<OP, 2, W>(a, stream);
+  if (per_lane <= 4) return launch_lut<OP, 4, W>(a, stream);
+  if (per_lane <= 6) return launch_lut<OP, 6, W>(a, stream);
+  return launch_lut<OP, 8, W>(a, stream);
 }
 
 template <int OP, int CH, int WPR>
