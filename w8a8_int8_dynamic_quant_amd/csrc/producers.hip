@@ -22,10 +22,10 @@
 //
 // fp32 evaluation (no contraction; correctly rounded division and square
 // root):
-//   LayerNorm: each lane sums its 8 CH values in order, a 64-lane butterfly
-//   adds the lanes (every lane ends with the same value) and the WPR wave
-//   sums are added in part order: no term passes through more than
-//   K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K
+//   LayerNorm: each lane sums its 8 CH values in order, a DPP reduction
+//   adds the lanes (six additions per term; one lane's total is used by
+//   every lane) and the WPR wave sums are added in part order: no term
+//   passes through more than K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K
 //   (squares accumulated by fused multiply-add), rstd = 1 / sqrt(var + eps),
 //   y = fma(fma(x, rstd, -(mean rstd)), 1 + scale, shift): two roundings
 //   fewer than the literal order, and the rounding of mean rstd is within
@@ -72,12 +72,23 @@ __device__ __forceinline__ void store16(uint4 v, __amdgpu_buffer_rsrc_t r, uint3
   __builtin_amdgcn_raw_buffer_store_b128((v4u){v.x, v.y, v.z, v.w}, r, off, 0, 0);
 }
 
-// Sum over the 64 lanes by a butterfly: at each step lanes i and i ^ off add
-// the same two values, so every lane ends with the same sum.
+// Sum over the 64 lanes: DPP within rows of 16 (xor 1, xor 2 in quads, then
+// rotations by 4 and 8), then lane 15 of each row into the next and lane 31
+// into the upper half; every term passes through six additions (as in a
+// butterfly) and the total is read from lane 63, so every lane returns the
+// same value. Every lane must be active. (The DPP source of a row left out
+// by the row mask reads 0, so those rows add nothing.)
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
-  return v;
+#define W8A8_DPP_ADD(ctrl, rows) \
+  v = v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rows, 0xF, false))
+  W8A8_DPP_ADD(0xB1, 0xF);     // quad [1,0,3,2]
+  W8A8_DPP_ADD(0x4E, 0xF);     // quad [2,3,0,1]
+  W8A8_DPP_ADD(0x124, 0xF);    // row_ror 4
+  W8A8_DPP_ADD(0x128, 0xF);    // row_ror 8
+  W8A8_DPP_ADD(0x142, 0xA);    // row_bcast 15
+  W8A8_DPP_ADD(0x143, 0xC);    // row_bcast 31
+#undef W8A8_DPP_ADD
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ void unpack8(uint4 v, float (&f)[8]) {
