@@ -15,17 +15,20 @@
 //     workgroup 0 also writes xq and a_scale out for the caller. The rows
 //     are requested before any weight window (a wave's loads complete in
 //     order, so rows requested behind its windows would arrive last). With
-//     at most two rows per wave (M <= 2W), the first kD0 windows follow the
-//     row loads at once, the wave quantises its rows as soon as they land,
-//     and only then requests its remaining windows: a wave that requests
-//     every window first stalls at issue once the CU's request queue is full,
-//     and its rows wait behind the stall (measured at M = 16 on 3072 ->
-//     18432: 16.1 us with every window first, 15.0 us with kD0 = 8);
+//     at most three rows per wave (M <= 3W; two with up to three token
+//     blocks), the first kD0 windows follow the row loads at once, the wave
+//     quantises its rows as soon as they land, and only then requests its
+//     remaining windows: a wave that requests every window first stalls at
+//     issue once the CU's request queue is full, and its rows wait behind
+//     the stall (measured at M = 16 on 3072 -> 18432: 16.1 us with every
+//     window first, 15.0 us with kD0 = 8; M = 17 / 24 / 32, whose rows were
+//     quantised before any window was requested: 19.1 / 19.9 / 22.5 ->
+//     16.0 / 17.6 / 21.4 us);
 //  2. the wave requests up to kD 128-byte windows of its rows at once
 //     (one buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte
 //     chunk l/8, so every instruction fetches 8 whole 128-byte lines).
 //     Each window is one v_mfma_i32_16x16x64_i8 per block of 8 tokens (up
-//     to 4 blocks). The loaded
+//     to 4 blocks, 3 for M <= 24). The loaded
 //     layout is the MFMA "A" layout if A-row i is read as weight row i%8 at
 //     chunk parity i/8: lane l holds A[l%16][k-group l/16] = row l%8, chunk
 //     2*(l/16) + (l/8)%2 = l/8. The "B" operand is built the same way from
@@ -50,12 +53,17 @@ constexpr int kQ = 6;                    // 16-byte chunks per lane per quantisa
 constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight at once
 
 // Work split of a launch: ONE_ROW: M <= W and K <= kShortK (a wave quantises
-// at most one activation row, overlapped with the weight stream); TWO_ROWS:
-// the same with up to two rows per wave (M <= 2W, M <= 16, bf16); SHORT: K <=
+// at most one activation row, overlapped with the weight stream); TWO_ROWS
+// and THREE_ROWS: the same with up to two or three rows per wave (M <= 2W
+// with up to three token blocks, M <= 3W with four); SHORT: K <=
 // kShortK, rows quantised before the stream; LONG: longer rows (read twice
-// for quantisation, weight windows refilled as they are consumed). Above 16
-// rows (four token blocks) only SHORT and LONG are used.
-enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3 };
+// for quantisation, weight windows refilled as they are consumed).
+enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3, THREE_ROWS = 4 };
+
+// activation rows a wave holds in registers across the first weight requests
+constexpr int rows_per_wave(int mode) {
+  return mode == ONE_ROW ? 1 : mode == TWO_ROWS ? 2 : mode == THREE_ROWS ? 3 : 0;
+}
 
 // LDS row stride for the quantised activations: K rounded up to whole
 // 128-byte windows plus 32 bytes. One quarter-wave of the "B" read takes 8
@@ -128,17 +136,18 @@ __device__ __forceinline__ float quantise_long(__amdgpu_buffer_rsrc_t rx, uint32
 }
 
 // Up to kMaxWaves waves per workgroup: three waves per SIMD. TB: blocks of 8
-// tokens (1, 2 or 4).
+// tokens (1 to 4).
 template <bool HAS_BIAS, int TB, int MODE, bool F16>
 __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(3, 8))) void small_m_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
     float* __restrict__ sa_out, int vec_flags, int G) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ float sa_lds[8 * TB];
-  // TWO_ROWS: the epilogue scales and biases of each wave's rows, parked
-  // here once they have landed (in registers across the stream they would
-  // make this mode spill)
-  __shared__ float scl_lds[MODE == TWO_ROWS ? kMaxWaves : 1][16];
+  // two or three rows per wave: the epilogue scales and biases of each
+  // wave's rows, parked here once they have landed (in registers across the
+  // stream they would make these modes spill)
+  constexpr int R = rows_per_wave(MODE);
+  __shared__ float scl_lds[R >= 2 ? kMaxWaves : 1][16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -179,22 +188,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   // ---- 1. activation quantisation into LDS, 2. weight requests ----
   // The K tail of each LDS row up to whole windows is never written: it only
   // meets weights that read as zero. Token rows >= M give unused columns.
-  if constexpr (MODE == ONE_ROW || MODE == TWO_ROWS) {
-    // rows wave (and wave + W with TWO_ROWS) in registers across the weight
-    // requests
-    constexpr bool R2 = MODE == TWO_ROWS;
-    const int m2 = wave + W;
-    uint4 v[kQ], v2[R2 ? kQ : 1];
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)wave * ldx, (uint32_t)K * 2u);
-    if (wave < M) {
+  if constexpr (R >= 1) {
+    // rows wave + W r (r < R) in registers across the first weight requests
+    uint4 v[R][kQ];
 #pragma unroll
-      for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
-    }
-    if constexpr (R2) {
-      const __amdgpu_buffer_rsrc_t rx2 =
-          make_rsrc(x + (int64_t)(m2 < M ? m2 : 0) * ldx, m2 < M ? (uint32_t)K * 2u : 0u);
+    for (int r = 0; r < R; ++r) {
+      const int m = wave + W * r;
+      if (r == 0 && wave >= M) continue;
+      // past M the descriptor is empty: the loads read zero
+      const __amdgpu_buffer_rsrc_t rx =
+          make_rsrc(x + (int64_t)(m < M ? m : 0) * ldx, m < M ? (uint32_t)K * 2u : 0u);
 #pragma unroll
-      for (int u = 0; u < kQ; ++u) v2[u] = load16(rx2, (uint32_t)(lane + 64 * u) * 16u);
+      for (int u = 0; u < kQ; ++u) v[r][u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
     }
     // the first kD0 weight requests go out right behind the row loads;
     // vmcnt(kD0) then waits for the rows only (loads complete in order)
@@ -203,27 +208,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
     for (int d = 0; d < kD0; ++d) buf[d] = wload(d);
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<kD0>();
-    if constexpr (R2) {
+    if constexpr (R >= 2) {
       if (lane < 8) {
         scl_lds[wave][lane] = sw1;
         scl_lds[wave][8 + lane] = bb1;
       }
     }
-    if (wave < M) {
-      const float s = quantise_regs<F16>(v, nchunks, lane, xs + wave * ldxs, xq_out + (int64_t)wave * K,
-                                    write_q);
-      if (lane == 0) {
-        sa_lds[wave] = s;
-        if (write_q) sa_out[wave] = s;
-      }
-    }
-    if constexpr (R2) {
-      if (m2 < M) {
-        const float s2 = quantise_regs<F16>(v2, nchunks, lane, xs + m2 * ldxs,
-                                            xq_out + (int64_t)m2 * K, write_q);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = wave + W * r;
+      if (m < M) {
+        const float s = quantise_regs<F16>(v[r], nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K,
+                                           write_q);
         if (lane == 0) {
-          sa_lds[m2] = s2;
-          if (write_q) sa_out[m2] = s2;
+          sa_lds[m] = s;
+          if (write_q) sa_out[m] = s;
         }
       }
     }
@@ -302,7 +301,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[t][r] = acc[t][r] + __builtin_amdgcn_ds_bpermute(src, acc[t][r]);
   float sw[4], bb[4];
-  if constexpr (MODE == TWO_ROWS) {
+  if constexpr (R >= 2) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       sw[r] = scl_lds[wave][4 * ((lane >> 4) & 1) + r];
@@ -357,24 +356,23 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   const int G = g.waves;
   const size_t lds = (size_t)(8 * TB) * (size_t)xs_stride(a.K);
   const int vf = epilogue_vec_flags(a);
-  if (a.K > kShortK)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, LONG, F16>), grid, block, lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vf, G);
-  else if (TB == 4)
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, SHORT, F16>), grid, block, lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vf, G);
-  else if (a.M <= threads / 64) {
-    if constexpr (TB < 4)
-      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, ONE_ROW, F16>), grid, block, lds, stream, x,
-                         ldx, a, xq_out, a_scale_out, vf, G);
-  } else if (!F16 && a.M <= 2 * (threads / 64)) {
-    // (bf16 only: the fp16 instantiation of this mode spills registers)
-    if constexpr (!F16 && TB < 4)
-      hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, TWO_ROWS, F16>), grid, block, lds, stream,
-                         x, ldx, a, xq_out, a_scale_out, vf, G);
-  } else
-    hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, SHORT, F16>), grid, block, lds, stream, x, ldx,
-                       a, xq_out, a_scale_out, vf, G);
+  // at most one, two or three activation rows per wave (three only with four
+  // token blocks), else the rows are quantised before the stream
+#define W8A8_SMALL_M(MODE)                                                                      \
+  hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, MODE, F16>), grid, block, lds, stream, x, ldx, \
+                     a, xq_out, a_scale_out, vf, G)
+  const int64_t waves = threads / 64;
+  if (a.K > kShortK) {
+    W8A8_SMALL_M(LONG);
+  } else if constexpr (TB == 4) {
+    if (a.M <= 3 * waves) W8A8_SMALL_M(THREE_ROWS);
+    else W8A8_SMALL_M(SHORT);
+  } else {
+    if (a.M <= waves) W8A8_SMALL_M(ONE_ROW);
+    else if (a.M <= 2 * waves) W8A8_SMALL_M(TWO_ROWS);
+    else W8A8_SMALL_M(SHORT);
+  }
+#undef W8A8_SMALL_M
   return hipGetLastError();
 }
 
@@ -382,11 +380,13 @@ template <bool F16>
 hipError_t launch_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
                         float* a_scale_out, hipStream_t stream) {
   if (a.bias) {
-    if (a.M > 16) return launch_variant<true, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+    if (a.M > 24) return launch_variant<true, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+    if (a.M > 16) return launch_variant<true, 3, F16>(x, ldx, a, xq_out, a_scale_out, stream);
     return a.M > 8 ? launch_variant<true, 2, F16>(x, ldx, a, xq_out, a_scale_out, stream)
                    : launch_variant<true, 1, F16>(x, ldx, a, xq_out, a_scale_out, stream);
   }
-  if (a.M > 16) return launch_variant<false, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  if (a.M > 24) return launch_variant<false, 4, F16>(x, ldx, a, xq_out, a_scale_out, stream);
+  if (a.M > 16) return launch_variant<false, 3, F16>(x, ldx, a, xq_out, a_scale_out, stream);
   return a.M > 8 ? launch_variant<false, 2, F16>(x, ldx, a, xq_out, a_scale_out, stream)
                  : launch_variant<false, 1, F16>(x, ldx, a, xq_out, a_scale_out, stream);
 }
