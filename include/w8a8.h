@@ -132,16 +132,14 @@ int w8a8_scaled_mm(const int8_t* xq, const float* a_scale, int64_t M, int64_t K,
  *     bytes, 16-byte aligned, owned by the caller. After the call it holds the
  *     quantised activations xq [M, K] int8 (row stride K) at byte offset 0 and
  *     a_scale [M] fp32 at byte offset W8A8_ALIGN256(M*K), on both paths.
- *     For shapes whose 256x256 tiles fill at most half of the compute units,
- *     or whose 128x128 tiles fill at most one round of them (N % 8 == 0,
- *     K above 896; w8a8_gemm_tile reports the tile), and for 64x64 tiles
- *     numbering up to two per compute unit (K of at least 1024), when the
- *     shape is not on the small-M path, the size also covers two to four
- *     slices of int32 partial sums after
- *     a_scale: the GEMM then splits K and a second kernel adds the
- *     partial sums before the epilogue (exact in int32, so the results are
- *     the same bits). The size depends on the current device's compute-unit
- *     count.
+ *     For shapes whose 128x128 tiles fill at most one round of the compute
+ *     units (N % 8 == 0, K above 896; w8a8_gemm_tile reports the tile), and
+ *     for 64x64 tiles numbering up to two per compute unit (K of at least
+ *     1024), when the shape is not on the small-M path, the size also covers
+ *     two to four slices of int32 partial sums after a_scale: the GEMM then
+ *     splits K and a second kernel adds the partial sums before the
+ *     epilogue (exact in int32, so the results are the same bits). The size
+ *     depends on the current device's compute-unit count.
  *   acc_debug [M, N] int32 or NULL, as in w8a8_scaled_mm.
  * Path: M <= W8A8_SMALL_M with K <= 8192, or M <= W8A8_SMALL_M_WIDE with
  * K <= 4096, runs one fused weight-streaming kernel that quantises x on chip; otherwise the activation quantisation

@@ -149,13 +149,15 @@ def test_workspace_and_path_queries():
     assert w8.gemm_tile(127, 3072, 16256) == (64, 64)
     assert w8.gemm_tile(127, 3072, 16384) == (128, 128)
     # split K (on a device of 256 compute units, the count assumed without a
-    # GPU): the workspace adds int32 partial sums after xq and a_scale
+    # GPU): the workspace adds int32 partial sums after xq and a_scale, on
+    # 128x128 and 64x64 tiles only (256x256 tiles that fill at most half of
+    # the compute units run as 128-row halves instead, with no partial sums)
     base = lambda M, K: ((M * K + 255) // 256) * 256 + ((4 * M + 255) // 256) * 256
-    assert w8.workspace_bytes(512, 4096, 12288) == base(512, 4096) + 2 * 512 * 12288 * 4
-    assert w8.workspace_bytes(700, 2000, 8200) == base(700, 2000) + 2 * 700 * 8200 * 4
+    assert w8.workspace_bytes(512, 4096, 12288) == base(512, 4096)      # 96 256x256 tiles
+    assert w8.workspace_bytes(700, 2000, 8200) == base(700, 2000)       # 99 256x256 tiles
     assert w8.workspace_bytes(512, 4096, 4096) == base(512, 4096) + 2 * 512 * 4096 * 4  # 128 tiles
     assert w8.workspace_bytes(1024, 4096, 4096) == base(1024, 4096) + 2 * 1024 * 4096 * 4
-    assert w8.workspace_bytes(1024, 4096, 4104) == base(1024, 4096) + 2 * 1024 * 4104 * 4  # 256 tiles
+    assert w8.workspace_bytes(1024, 4096, 4104) == base(1024, 4096)     # 68 256x256 tiles
     assert w8.workspace_bytes(256, 3072, 18432) == base(256, 3072)      # 288 128x128 tiles
     assert w8.workspace_bytes(64, 3072, 18432) == base(64, 3072) + 3 * 64 * 18432 * 4
     assert w8.workspace_bytes(64, 4096, 4096) == base(64, 4096) + 4 * 64 * 4096 * 4
@@ -164,7 +166,7 @@ def test_workspace_and_path_queries():
     assert w8.workspace_bytes(40, 960, 1024) == base(40, 960)           # K too short
     assert w8.workspace_bytes(32, 3072, 18432) == base(32, 3072)        # small-M path
     assert w8.workspace_bytes(4352, 3072, 9216) == base(4352, 3072)      # enough tiles
-    assert w8.workspace_bytes(512, 4096, 12296) == base(512, 4096) + 2 * 512 * 12296 * 4
+    assert w8.workspace_bytes(512, 4096, 12296) == base(512, 4096)      # 98 256x256 tiles
     assert w8.workspace_bytes(512, 4096, 12292) == base(512, 4096)       # N % 8 != 0
     assert w8.workspace_bytes(512, 768, 12288) == base(512, 768)         # K too short
 

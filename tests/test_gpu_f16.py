@@ -194,11 +194,26 @@ def test_f16_256_tile_with_bias(N):
 
 def test_f16_linear_split_k():
     """fp16 output and bias through the split-K reduction (see the bf16 test)."""
-    M, N, K = 700, 8200, 2000
+    M, N, K = 512, 4104, 2000
+    assert w8.gemm_tile(M, K, N) == (128, 128)
     assert w8.workspace_bytes(M, K, N) > M * K + 4 * M + 512
     rng = np.random.default_rng(41)
     x = random_f16(rng, (M, K))
     w = random_f16(rng, (N, K), 0.02)
     b = random_f16(rng, (N,), 0.01)
     announce(f"fp16 split-K linear M={M} N={N} K={K}")
+    _linear_case(x, w, b)
+
+
+def test_f16_linear_256_tile_halves():
+    """fp16 output and bias with every 256x256 tile run as two 128-row halves
+    (99 tiles, at most half of the compute units)."""
+    M, N, K = 700, 8200, 2000
+    assert w8.gemm_tile(M, K, N) == (256, 256)
+    assert w8.workspace_bytes(M, K, N) < M * K + 4 * M + 512
+    rng = np.random.default_rng(43)
+    x = random_f16(rng, (M, K))
+    w = random_f16(rng, (N, K), 0.02)
+    b = random_f16(rng, (N,), 0.01)
+    announce(f"fp16 256 tile halves M={M} N={N} K={K}")
     _linear_case(x, w, b)

@@ -1,8 +1,9 @@
 """w8a8_linear and the fused GELU producer captured in a HIP graph
 (torch.cuda.graph) and replayed.
 
-Every path (the small-M kernel, quantisation + GEMM, K split on each tile
-size with its reduction kernel) launches only kernels on the caller's stream,
+Every path (the small-M kernel, quantisation + GEMM, 256x256 tiles run as
+halves, K split on 128x128 and 64x64 tiles with its reduction kernel)
+launches only kernels on the caller's stream,
 with no allocation, copy or memset, so a graph holds the whole linear. Each
 replay follows new activations copied into the captured input and is compared
 bit for bit with an eager call on the same activations, with eager work and
@@ -33,7 +34,7 @@ def _gpu():
     (300, 700, 1296, True),      # quantisation + GEMM, one pass
     (64, 4096, 4096, True),      # 64x64 tiles, K split in four
     (512, 4096, 4096, False),    # 128x128 tiles, K split in two
-    (512, 12288, 4096, True),    # 256x256 tiles, K split in two
+    (512, 12288, 4096, True),    # 256x256 tiles, every tile as two 128-row halves
 ])
 def test_linear_graph_replays(M, N, K, with_bias):
     rng = np.random.default_rng(M * 7 + N + K)

@@ -329,13 +329,16 @@ def test_linear_256_tile_store_paths(N, with_bias):
 
 
 def _pp_halves(M, N):
-    """True when the 256x256 kernel runs the last round of some XCD's tiles
-    as 128-row halves (the rule the launcher applies: per XCD of cus/8
-    compute units, tiles beyond whole rounds, when at most half a round)."""
+    """True when the 256x256 kernel runs some tiles as 128-row halves (the
+    rule the launcher applies, per XCD of cus/8 compute units: every tile
+    when the XCD's tiles fill at most half of them, else the tiles beyond
+    whole rounds when they fill at most half a round)."""
     cpx = torch.cuda.get_device_properties(0).multi_processor_count // 8
     T = -(-M // 256) * -(-N // 256)
     for x in range(8):
         tx = T // 8 + (1 if x < T % 8 else 0)
+        if 0 < tx and 2 * tx <= cpx:
+            return True
         rem = tx % cpx if tx > cpx else 0
         if 0 < rem and 2 * rem <= cpx:
             return True
@@ -343,11 +346,16 @@ def _pp_halves(M, N):
 
 
 @pytest.mark.parametrize("M,N,K,with_bias", [(4152, 9224, 272, True), (4100, 9218, 272, False),
-                                             (4352, 9220, 1040, True), (4352, 12288, 208, False)])
+                                             (4352, 9220, 1040, True), (4352, 12288, 208, False),
+                                             (512, 12288, 4096, True), (700, 8200, 2000, True),
+                                             (520, 10240, 1040, False), (516, 8196, 528, True)])
 def test_linear_256_tile_halves(M, N, K, with_bias):
-    """Tiles of the last round split into 128-row halves: a last M tile whose
-    second half is empty (4100: 4 rows in the first) or ragged (4152), the
-    three store paths (N % 8 == 0, N % 4 == 0, else) and a K tail."""
+    """Tiles split into 128-row halves: in the last round (the 4352-row
+    shapes: a last M tile whose second half is empty (4100: 4 rows in the
+    first) or ragged (4152), the three store paths (N % 8 == 0, N % 4 == 0,
+    else) and a K tail), and every tile of shapes whose tiles fill at most
+    half of the compute units (M = 516: a last M tile of 4 rows, whose second
+    half is empty; N % 8 == 4)."""
     assert w8.gemm_tile(M, K, N) == (256, 256)
     assert _pp_halves(M, N)
     rng = np.random.default_rng(M + N + K)
@@ -358,14 +366,12 @@ def test_linear_256_tile_halves(M, N, K, with_bias):
     print(_linear_case(x, w, b)[0])
 
 
-# Split K: shapes whose 256x256 tiles fill at most half of the compute units
-# or whose 128x128 tiles fill at most one round (K split in two), and skinny
-# shapes on 64x64 tiles (K split in up to four); w8a8_linear then splits K
-# (its workspace holds the partial sums), w8a8_scaled_mm does not. Both must
-# give the oracle's acc and the same y bits. (K = 1040 / 2064: the last split
-# ends on a 16-byte tail.)
-@pytest.mark.parametrize("M,N,K,with_bias", [(512, 12288, 4096, True), (700, 8200, 2000, True),
-                                             (520, 10240, 1040, False), (512, 4096, 4096, False),
+# Split K: shapes whose 128x128 tiles fill at most one round (K split in
+# two), and skinny shapes on 64x64 tiles (K split in up to four);
+# w8a8_linear then splits K (its workspace holds the partial sums),
+# w8a8_scaled_mm does not. Both must give the oracle's acc and the same y
+# bits. (K = 1040 / 2064: the last split ends on a 16-byte tail.)
+@pytest.mark.parametrize("M,N,K,with_bias", [(512, 4096, 4096, False),
                                              (200, 2056, 1040, True), (1024, 2056, 2064, True),
                                              (64, 18432, 3072, True), (40, 1032, 2064, True),
                                              (100, 2056, 4096, False), (100, 18432, 3072, True)])
@@ -386,8 +392,9 @@ def test_linear_split_k(M, N, K, with_bias):
 
 
 def test_linear_split_k_fallback_on_unaligned_output():
-    """An output row stride that is not a multiple of 8 takes the one-pass GEMM."""
-    M, N, K = 512, 12288, 2048
+    """An output row stride that is not a multiple of 8 takes the one-pass GEMM
+    (a shape whose 128x128 tiles split K otherwise)."""
+    M, N, K = 512, 4096, 2048
     rng = np.random.default_rng(5)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)

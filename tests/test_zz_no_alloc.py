@@ -52,8 +52,8 @@ def _run_pair(M, K, N, with_bias, seed):
 
 
 @pytest.mark.parametrize("first,second", [
-    # K split in two on 256x256 tiles (partial sums in the scratch), then a one-pass GEMM
-    ((512, 4096, 12288, True), (300, 1040, 700, False)),
+    # K split in two on 128x128 tiles (partial sums in the scratch), then a one-pass GEMM
+    ((512, 4096, 4096, True), (300, 1040, 700, False)),
     # one-pass GEMM, then the fused small-M kernel
     ((1024, 3072, 3072, False), (8, 3072, 1024, True)),
     # small-M, then a smaller small-M

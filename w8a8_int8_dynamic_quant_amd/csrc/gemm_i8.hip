@@ -96,21 +96,30 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int& tm, i
   tn = r / gm;
 }
 
+// Whole tiles of an XCD's run of tx tiles over its cpx compute units (cpx
+// = 0: all whole): all of them but the last round when that round is at
+// most half full, none when the whole run is (its tiles then run as
+// halves, twice as many pieces of half the work, instead of as a split K).
+__host__ __device__ inline int pp_whole_tiles(int tx, int cpx) {
+  if (cpx <= 0) return tx;
+  if (2 * tx <= cpx) return 0;
+  const int rem = tx > cpx ? tx % cpx : 0;
+  return (rem > 0 && 2 * rem <= cpx) ? tx - rem : tx;
+}
+
 // Block -> tile for the ping-pong kernel. XCD x (blockIdx & 7; the hardware
 // hands workgroups to the XCDs in turn) takes the same contiguous run of
-// tiles as tile_coords, in dispatch order. When cpx > 0 and the last round
-// of that run over the XCD's cpx compute units is at most half full, its
-// last tiles are split into two 128-row halves (half = 0, 1), numbered after
-// the whole tiles (half = -1), so the last round runs twice as many pieces
-// of half the work. Returns false for a block past its XCD's pieces.
+// tiles as tile_coords, in dispatch order. Beyond the run's whole tiles
+// (pp_whole_tiles), each tile is split into two 128-row halves (half = 0,
+// 1), numbered after the whole tiles (half = -1). Returns false for a
+// block past its XCD's pieces.
 __device__ __forceinline__ bool tile_coords_halves(int tiles_m, int tiles_n, int cpx, int& tm,
                                                    int& tn, int& half) {
   const int T = tiles_m * tiles_n;
   const int b = blockIdx.x;
   const int xcd = b & 7, local = b >> 3;
   const int tx = (T >> 3) + (xcd < (T & 7) ? 1 : 0);
-  const int rem = (cpx > 0 && tx > cpx) ? tx % cpx : 0;
-  const int whole = (rem > 0 && 2 * rem <= cpx) ? tx - rem : tx;
+  const int whole = pp_whole_tiles(tx, cpx);
   int t = xcd * (T >> 3) + min(xcd, T & 7);
   half = -1;
   if (local < whole) {
@@ -620,7 +629,7 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
 // requests for rows 128.. of the xq panel read out of bounds (no memory
 // traffic, zeros into LDS rows nothing reads), so every wait keeps its
 // constant.
-template <bool HAS_BIAS, bool F16, bool SPLIT, int FM>
+template <bool HAS_BIAS, bool F16, int FM>
 __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n0, int vec_flags,
                                         int kps, int8_t* lds0, int8_t* lds1, int8_t* lds2,
                                         int8_t* lds3, float* lds_sa, float* lds_sw, float* lds_b) {
@@ -763,26 +772,6 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   wait_vmcnt<0>();
   __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (SPLIT) {
-    const __amdgpu_buffer_rsrc_t r_p =
-        make_rsrc(a.partial + ((int64_t)blockIdx.y * M + m0) * N + n0,
-                  (uint32_t)(((int64_t)(rows_x - 1) * N + rows_w) * 4));
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int ml = 32 * FM * grp + 32 * j + frag_row;
-        const v16i& c = acc[i][j];
-        const v4i run[4] = {c.lo.lo, c.lo.hi, c.hi.lo, c.hi.hi};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int nl = 64 * wn + 32 * i + 8 * q + 4 * frag_half;
-          const uint32_t o = (nl < (int)rows_w) ? (uint32_t)(ml * N + nl) * 4u : kOOB;
-          __builtin_amdgcn_raw_buffer_store_b128(run[q], r_p, o, 0, 0);
-        }
-      }
-    return;
-  }
   // Staging, 8 KiB per wave (half the sub-tile at a time), in a buffer that
   // no request still in flight targets. With n = ke - kb stages, the last
   // requests (of stages n, n+1, n+2, relative to kb) target buffers
@@ -797,9 +786,8 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
                                          n0, rows_x, rows_w, grp, wn, lane, vec_flags);
 }
 
-// cpx: compute units per XCD when the last round of each XCD's tiles may be
-// split into halves (0: never).
-template <bool HAS_BIAS, bool F16, bool SPLIT>
+// cpx: compute units per XCD when tiles may be split into halves (0: never).
+template <bool HAS_BIAS, bool F16>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
                                                         int vec_flags, int kps, int cpx) {
   constexpr int HALF = 256 * 64;
@@ -813,13 +801,13 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, i
   int tm, tn, half;
   if (!tile_coords_halves(tiles_m, tiles_n, cpx, tm, tn, half)) return;
   if (half < 0) {
-    pp_tile<HAS_BIAS, F16, SPLIT, 4>(a, (int64_t)tm * 256, (int64_t)tn * 256, vec_flags, kps, lds0,
-                                     lds1, lds2, lds3, lds_sa, lds_sw, lds_b);
-  } else if constexpr (!SPLIT) {
+    pp_tile<HAS_BIAS, F16, 4>(a, (int64_t)tm * 256, (int64_t)tn * 256, vec_flags, kps, lds0, lds1,
+                              lds2, lds3, lds_sa, lds_sw, lds_b);
+  } else {
     const int64_t m0 = (int64_t)tm * 256 + 128 * half;
     if (m0 < a.M)
-      pp_tile<HAS_BIAS, F16, SPLIT, 2>(a, m0, (int64_t)tn * 256, vec_flags, kps, lds0, lds1, lds2,
-                                       lds3, lds_sa, lds_sw, lds_b);
+      pp_tile<HAS_BIAS, F16, 2>(a, m0, (int64_t)tn * 256, vec_flags, kps, lds0, lds1, lds2, lds3,
+                                lds_sa, lds_sw, lds_b);
   }
 }
 
@@ -889,41 +877,36 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream, int splits = 1, int
   return hipGetLastError();
 }
 
-// Blocks of the ping-pong kernel for T tiles with the last round of each
-// XCD's run split into halves where tile_coords_halves does so (cpx compute
-// units per XCD): 8 times the largest number of pieces of one XCD.
+// Blocks of the ping-pong kernel for T tiles, with tiles split into halves
+// where tile_coords_halves does so (cpx compute units per XCD): 8 times the
+// largest number of pieces of one XCD.
 int64_t pp_blocks(int64_t T, int cpx) {
   int64_t most = 0;
   for (int x = 0; x < 8; ++x) {
-    const int64_t tx = (T >> 3) + (x < (T & 7) ? 1 : 0);
-    const int64_t rem = (cpx > 0 && tx > cpx) ? tx % cpx : 0;
-    const int64_t whole = (rem > 0 && 2 * rem <= cpx) ? tx - rem : tx;
-    most = std::max(most, whole + 2 * (tx - whole));
+    const int tx = (int)((T >> 3) + (x < (T & 7) ? 1 : 0));
+    const int whole = pp_whole_tiles(tx, cpx);
+    most = std::max<int64_t>(most, whole + 2 * (tx - whole));
   }
   return 8 * most;
 }
 
-// 256 x 256 tiles: the eight-wave ping-pong kernel (kps counts 128-byte
-// stages, as the split-K plan does). Without split K, the last round of
-// each XCD's tiles runs as 128-row halves when it is at most half full
+// 256 x 256 tiles: the eight-wave ping-pong kernel. The last round of each
+// XCD's tiles runs as 128-row halves when it is at most half full
 // (4352 x 3072 x 9216, 612 tiles: 76 or 77 per XCD of 32 compute units,
-// so 12 or 13 tiles in the last round become 24 or 26 halves).
-hipError_t launch_pp(const GemmArgs& a, hipStream_t stream, int splits = 1, int kps = 0) {
+// so 12 or 13 tiles in the last round become 24 or 26 halves), and every
+// tile does when all of them fill at most half of the compute units
+// (512 x 4096 x 12288: 96 tiles, 192 halves, 46.7 -> 42.1 us per product;
+// K split in two with a reduction kernel took 51 us).
+hipError_t launch_pp(const GemmArgs& a, hipStream_t stream) {
   constexpr int T = 256, BK = 64;
   const int64_t tiles_m = (a.M + T - 1) / T, tiles_n = (a.N + T - 1) / T;
   const int vec_flags = epilogue_vec_flags(a);
-  kps = splits == 1 ? (int)((a.K + BK - 1) / BK) : 2 * kps;
-  if (splits > 1) {
-    const dim3 grid((unsigned)(tiles_m * tiles_n), (unsigned)splits), block(512);
-    hipLaunchKernelGGL((gemm_pp_kernel<false, false, true>), grid, block, 0, stream, a,
-                       (int)tiles_m, (int)tiles_n, vec_flags, kps, 0);
-    return hipGetLastError();
-  }
+  const int kps = (int)((a.K + BK - 1) / BK);
   const int cus = device_cus();
   const int cpx = cus % 8 == 0 ? cus / 8 : 0;
   const dim3 grid((unsigned)pp_blocks(tiles_m * tiles_n, cpx)), block(512);
-#define W8A8_PP(B, H)                                                                           \
-  hipLaunchKernelGGL((gemm_pp_kernel<B, H, false>), grid, block, 0, stream, a, (int)tiles_m, \
+#define W8A8_PP(B, H)                                                                    \
+  hipLaunchKernelGGL((gemm_pp_kernel<B, H>), grid, block, 0, stream, a, (int)tiles_m, \
                      (int)tiles_n, vec_flags, kps, cpx)
   if (a.f16) {
     if (a.bias) W8A8_PP(true, true);
@@ -937,20 +920,19 @@ hipError_t launch_pp(const GemmArgs& a, hipStream_t stream, int splits = 1, int 
 }
 
 // Split-K plan for a shape: K is split in two (with K of at least 8 stages)
-// when the chosen tiles leave compute units idle: 256x256 tiles filling at
-// most half of them, or 128x128 tiles filling at most one round (two 64 KiB
+// when 128x128 tiles fill at most one round of the compute units (two 64 KiB
 // 128x128 workgroups share a CU, so the split pairs overlap). Measured:
-// 512x4096x12288 (256 tiles) 58 -> 53-55 us; 512x4096x4096 41 -> 31 us,
-// 1024x4096x4096 49 -> 40 us, 512x4096x8192 49 -> 40 us (128 tiles). More
-// splits lose: each adds a slice of int32 partial sums, written and read back
-// (512x4096x4096 split 8 ways on 256 tiles: 43 us), except on 64x64 tiles,
-// whose skinny products wait on the weight stream: up to four pieces there
+// 512x4096x4096 41 -> 31 us, 1024x4096x4096 49 -> 40 us, 512x4096x8192
+// 49 -> 40 us (128 tiles). More splits lose: each adds a slice of int32
+// partial sums, written and read back, except on 64x64 tiles, whose skinny
+// products wait on the weight stream: up to four pieces there
 // (64x3072x18432: 34 -> 30 us in three, 64x4096x4096: 34 -> 19 us in four).
-// splits = 1: no split.
+// 256x256 tiles that fill at most half of the compute units run as halves
+// instead (launch_pp), with no partial sums. splits = 1: no split.
 struct SplitPlan {
   int splits = 1;
   int kps = 0;              // K stages per split
-  int tile = 256;           // BM = BN of the split GEMM
+  int tile = 128;           // BM = BN of the split GEMM (128 or 64)
 };
 
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
@@ -972,7 +954,7 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
   }
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   const int64_t nk = (K + 127) / 128;
-  if ((bm == 128 ? tiles : 2 * tiles) > device_cus() || nk < 8) return p;
+  if (bm != 128 || tiles > device_cus() || nk < 8) return p;
   p.tile = bm;
   p.kps = (int)((nk + 1) / 2);
   p.splits = (int)((nk + p.kps - 1) / p.kps);
@@ -1019,9 +1001,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     const int vf = epilogue_vec_flags(a);
     const SplitPlan p = split_plan(a.M, a.N, a.K);
     if (p.splits > 1 && (vf & 4) && (!a.acc_debug || (vf & 2))) {
-      if (hipError_t e = p.tile == 256   ? launch_pp(a, stream, p.splits, p.kps)
-                         : p.tile == 128 ? launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
-                                         : launch_cfg<64, 64, 2, 2, 64, 2>(a, stream, p.splits, p.kps);
+      if (hipError_t e = p.tile == 128 ? launch_cfg<128, 128, 2, 2, 128, 2>(a, stream, p.splits, p.kps)
+                                       : launch_cfg<64, 64, 2, 2, 64, 2>(a, stream, p.splits, p.kps);
           e != hipSuccess)
         return e;
       const int64_t groups = a.M * (a.N >> 3);
