@@ -55,10 +55,10 @@ constexpr int64_t kShortK = 128 * kD;    // K up to this: every window in flight
 // Work split of a launch: ONE_ROW: M <= W and K <= kShortK (a wave quantises
 // at most one activation row, overlapped with the weight stream); TWO_ROWS
 // and THREE_ROWS: the same with up to two or three rows per wave (M <= 2W
-// with up to three token blocks, M <= 3W with four); SHORT: K <=
-// kShortK, rows quantised before the stream; LONG: longer rows (read twice
-// for quantisation, weight windows refilled as they are consumed).
-enum Mode { ONE_ROW = 0, SHORT = 1, LONG = 2, TWO_ROWS = 3, THREE_ROWS = 4 };
+// with up to three token blocks, M <= 3W with four); LONG: K > kShortK,
+// rows read twice for quantisation before the stream, weight windows
+// refilled as they are consumed.
+enum Mode { ONE_ROW = 0, LONG = 2, TWO_ROWS = 3, THREE_ROWS = 4 };
 
 // activation rows a wave holds in registers across the first weight requests
 constexpr int rows_per_wave(int mode) {
@@ -235,15 +235,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   } else {
     for (int m = wave; m < M; m += W) {
       const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + (int64_t)m * ldx, (uint32_t)K * 2u);
-      float s;
-      if constexpr (MODE == SHORT) {
-        uint4 v[kQ];
-#pragma unroll
-        for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
-        s = quantise_regs<F16>(v, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
-      } else {
-        s = quantise_long<F16>(rx, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
-      }
+      const float s =
+          quantise_long<F16>(rx, nchunks, lane, xs + m * ldxs, xq_out + (int64_t)m * K, write_q);
       if (lane == 0) {
         sa_lds[m] = s;
         if (write_q) sa_out[m] = s;
@@ -357,7 +350,7 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   const size_t lds = (size_t)(8 * TB) * (size_t)xs_stride(a.K);
   const int vf = epilogue_vec_flags(a);
   // at most one, two or three activation rows per wave (three only with four
-  // token blocks), else the rows are quantised before the stream
+  // token blocks); every M the launcher sends here fits (see launch_dtype)
 #define W8A8_SMALL_M(MODE)                                                                      \
   hipLaunchKernelGGL((small_m_kernel<HAS_BIAS, TB, MODE, F16>), grid, block, lds, stream, x, ldx, \
                      a, xq_out, a_scale_out, vf, G)
@@ -365,16 +358,21 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   if (a.K > kShortK) {
     W8A8_SMALL_M(LONG);
   } else if constexpr (TB == 4) {
-    if (a.M <= 3 * waves) W8A8_SMALL_M(THREE_ROWS);
-    else W8A8_SMALL_M(SHORT);
+    if (a.M > 3 * waves) return hipErrorInvalidValue;
+    W8A8_SMALL_M(THREE_ROWS);
   } else {
+    if (a.M > 2 * waves) return hipErrorInvalidValue;
     if (a.M <= waves) W8A8_SMALL_M(ONE_ROW);
-    else if (a.M <= 2 * waves) W8A8_SMALL_M(TWO_ROWS);
-    else W8A8_SMALL_M(SHORT);
+    else W8A8_SMALL_M(TWO_ROWS);
   }
 #undef W8A8_SMALL_M
   return hipGetLastError();
 }
+
+// Token blocks by M (launch_dtype) against the rows the row modes hold: one
+// block (M <= 8) on at least kMinWaves waves, two or three on kMaxWaves.
+static_assert(8 <= 2 * kMinWaves && 24 <= 2 * kMaxWaves && kSmallMWideRows <= 3 * kMaxWaves,
+              "every small-M row count fits a row mode");
 
 template <bool F16>
 hipError_t launch_dtype(const uint16_t* x, int64_t ldx, const GemmArgs& a, int8_t* xq_out,
