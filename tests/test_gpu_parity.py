@@ -294,15 +294,16 @@ def test_linear_subnormal_scales_and_outputs():
 
 @pytest.mark.parametrize("M,N,K", [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040),
                                    (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088), (13, 18432, 3072),
-                                   (17, 70, 1040), (25, 200, 3072), (32, 18432, 3072),
-                                   (24, 70, 3088), (32, 33, 4096)])
+                                   (17, 70, 1040), (20, 200, 3072), (25, 200, 3072), (28, 70, 1040),
+                                   (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)])
 def test_linear_small_m_work_splits(M, N, K):
     """Every way the small-M kernel splits the activation rows over its waves
     (W = 4 waves for N = 33, 70 and 200 and 9 for N = 18432 up to M = 8, 12
-    from M = 9 on): one row per wave (M <= W), two rows per wave held across
-    the weight requests (W < M <= 16), rows quantised before the stream
-    (every M above 16; fp16 above W, in the fp16 tests) and rows longer than
-    the register-resident limit (K > 3072)."""
+    from M = 9 on), each row held in registers across the wave's first weight
+    requests: one row per wave (M <= W), two (W < M <= 2W: up to 16 rows on
+    two token blocks, 17-24 on three) and three (25-32 rows, four token
+    blocks); and rows longer than the register-resident limit (K > 3072),
+    read twice and quantised before the stream."""
     rng = np.random.default_rng(M * 31 + N + K)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)
