@@ -313,6 +313,43 @@ def test_linear_small_m_work_splits(M, N, K):
     print(_linear_case(x, w, b)[0])
 
 
+def _tie_rows(rng, M, K):
+    """bf16 rows whose quantisation meets rounding ties: amax 127 * 2^e gives
+    the scale 2^e exactly, so every x = (k + 1/2) 2^e (|k + 1/2| <= 62.5,
+    seven significant bits, exact in bf16) has x / s exactly half-way between
+    two codes (round half to even decides); rows with a subnormal scale
+    (every element takes the division); and plain rows between them."""
+    rows = []
+    for r in range(M):
+        kind = r % 3
+        if kind == 0:
+            e = int(rng.integers(-10, 10))
+            v = (rng.integers(-63, 63, K) + 0.5) * 2.0 ** e
+            v[int(rng.integers(0, K))] = 127.0 * 2.0 ** e * (1 if rng.random() < 0.5 else -1)
+        elif kind == 1:
+            v = rng.standard_normal(K) * 2.0 ** -133
+        else:
+            v = rng.standard_normal(K)
+        rows.append(to_bf16_bits(v))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 72, 3072), (5, 72, 3072), (12, 200, 3072), (16, 200, 3072),
+                                   (20, 200, 3072), (30, 200, 3072), (9, 200, 4112)])
+def test_linear_small_m_rounding_ties(M, N, K):
+    """The fused small-M kernel's on-chip quantisation on rows full of exact
+    rounding ties and on rows with subnormal scales, in each way it holds the
+    rows (one, two, three per wave; K > 3072: read twice): codes and scales
+    bit-exact against the oracle (which rounds fl32(x / s) half to even)."""
+    assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
+    rng = np.random.default_rng(M * 101 + K)
+    x = _tie_rows(rng, M, K)
+    w = random_bf16(rng, (N, K), 0.02)
+    b = random_bf16(rng, (N,), 0.01)
+    announce(f"small-M rounding ties M={M} N={N} K={K}")
+    print(_linear_case(x, w, b)[0])
+
+
 @pytest.mark.parametrize("N", [2056, 2052, 2050])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_linear_256_tile_store_paths(N, with_bias):
