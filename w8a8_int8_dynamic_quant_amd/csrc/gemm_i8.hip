@@ -28,6 +28,12 @@
 // * Four-wave kernel: a two-stage LDS ring; loads for stage kt+1 are issued
 //   right after the barrier of stage kt; one barrier per stage; the wait
 //   before it only counts this stage's loads (exact s_waitcnt vmcnt).
+// * Filling the chip: 256 x 256 tiles run whole or as two 128-row halves
+//   (the last round of an XCD's tiles when it is at most half full, every
+//   tile when all of them fill at most half of the compute units; one
+//   launch either way). K is split only on 128 x 128 and 64 x 64 tiles, with
+//   int32 partial sums in the caller's workspace and a second kernel that
+//   adds them before the epilogue.
 // * Out-of-range rows read as zeros through the buffer descriptor's bound;
 //   K-tail chunks are sent out of bounds, so ragged M, N and K need no branch.
 // * Output stores are non-temporal, so the output does not evict the panels
