@@ -386,14 +386,15 @@ def _pp_halves(M, N):
 @pytest.mark.parametrize("M,N,K,with_bias", [(4152, 9224, 272, True), (4100, 9218, 272, False),
                                              (4352, 9220, 1040, True), (4352, 12288, 208, False),
                                              (512, 12288, 4096, True), (700, 8200, 2000, True),
-                                             (520, 10240, 1040, False), (516, 8196, 528, True)])
+                                             (520, 10240, 1040, False), (516, 8196, 528, True),
+                                             (516, 8194, 528, False)])
 def test_linear_256_tile_halves(M, N, K, with_bias):
     """Tiles split into 128-row halves: in the last round (the 4352-row
     shapes: a last M tile whose second half is empty (4100: 4 rows in the
     first) or ragged (4152), the three store paths (N % 8 == 0, N % 4 == 0,
     else) and a K tail), and every tile of shapes whose tiles fill at most
     half of the compute units (M = 516: a last M tile of 4 rows, whose second
-    half is empty; N % 8 == 4)."""
+    half is empty; N % 8 == 4 and N % 4 == 2)."""
     assert w8.gemm_tile(M, K, N) == (256, 256)
     assert _pp_halves(M, N)
     rng = np.random.default_rng(M + N + K)
