@@ -114,7 +114,8 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None):
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (3, 5, 48), (16, 70, 8192), (2, 129, 8208),
                                    (40, 72, 4112), (20, 40, 8192), (3, 40, 24592), (2, 24, 32768),
-                                   (17, 33, 64), (25, 70, 1040), (32, 200, 3072), (65, 129, 1040),
+                                   (17, 33, 64), (25, 70, 1040), (32, 200, 3072), (13, 18432, 1024),
+                                   (20, 18432, 1024), (32, 18432, 1024), (65, 129, 1040),
                                    (257, 513, 256), (300, 700, 1296)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_f16_linear_shapes(M, N, K, with_bias):

@@ -292,23 +292,55 @@ def test_linear_subnormal_scales_and_outputs():
         assert np.any((np.abs(y) > 0) & (np.abs(y) < np.finfo(np.float32).tiny))
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040),
-                                   (12, 18432, 3072), (16, 200, 3072), (6, 70, 3088), (13, 18432, 3072),
-                                   (17, 70, 1040), (20, 200, 3072), (25, 200, 3072), (28, 70, 1040),
-                                   (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)])
+def _small_m_form(M, K, N, cus=256):
+    """Which small-M kernel form serves (M, K, N) on a 256-CU device, by the
+    launcher's rule: the weight waves G = clamp(ceil(ceil(N/8) / cus), 4, 12);
+    the quantiser waves H (one per row up to 4 rows, else a multiple of 4 that
+    fits beside G in 16 waves, at most M); the split kernel for K > 3072 or
+    above 8 rows with at most three rows per quantiser, the row modes
+    otherwise. Returns (kernel, detail)."""
+    G = min(12, max(4, -(-(-(-N // 8)) // cus)))
+    H = M if M <= 4 else min(M, 4 * min(-(-M // 4), (16 - G) // 4))
+    TB = -(-M // 8)
+    if K > 3072 or (M > 8 and -(-M // H) <= 3):
+        depth = {1: 24, 2: 24, 3: 16, 4: 12}[TB]
+        return "split", ("long rows" if K > 3072 else
+                         "refill" if K > 128 * depth else "whole"), TB
+    W = 12 if TB >= 2 else G
+    return "rows", ("one" if M <= W and TB == 1 else "three" if TB == 4 else "two"), TB
+
+
+_WORK_SPLITS = [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040), (12, 18432, 3072),
+                (16, 200, 3072), (3, 72, 4112), (6, 70, 3088), (10, 72, 5136), (13, 18432, 3072),
+                (17, 70, 1040), (20, 200, 3072), (20, 18432, 2048), (25, 200, 3072), (28, 70, 1040),
+                (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)]
+
+
+def test_small_m_work_splits_cover_every_form():
+    """The parity cases below reach every form of both small-M kernels."""
+    forms = {_small_m_form(M, K, N) for (M, N, K) in _WORK_SPLITS}
+    want = {("rows", "one", 1), ("rows", "two", 1), ("rows", "two", 2), ("rows", "two", 3),
+            ("rows", "three", 4)}
+    want |= {("split", "long rows", tb) for tb in (1, 2, 3, 4)}
+    want |= {("split", "whole", tb) for tb in (2, 3, 4)}
+    want |= {("split", "refill", tb) for tb in (3, 4)}
+    assert want <= forms, want - forms
+
+
+@pytest.mark.parametrize("M,N,K", _WORK_SPLITS)
 def test_linear_small_m_work_splits(M, N, K):
-    """Every way the small-M kernel splits the activation rows over its waves
-    (W = 4 waves for N = 33, 70 and 200 and 9 for N = 18432 up to M = 8, 12
-    from M = 9 on), each row held in registers across the wave's first weight
-    requests: one row per wave (M <= W), two (W < M <= 2W: up to 16 rows on
-    two token blocks, 17-24 on three) and three (25-32 rows, four token
-    blocks); and rows longer than the register-resident limit (K > 3072),
-    read twice and quantised before the stream."""
+    """Every form of the two small-M kernels (test above): row modes, where
+    each wave holds one, two or three rows in registers across its first
+    weight requests (W = 4 waves for N = 33, 70, 72 and 200 and 9 for
+    N = 18432 up to M = 8, 12 from M = 9 on); split roles, where quantiser
+    waves without weight rows quantise rows held in registers (K <= 3072)
+    or read twice from memory (longer rows) while the weight waves stream,
+    with all of a row group's windows in flight or refilled as consumed."""
     rng = np.random.default_rng(M * 31 + N + K)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)
     b = random_bf16(rng, (N,), 0.01)
-    announce(f"small-M work split M={M} N={N} K={K}")
+    announce(f"small-M work split M={M} N={N} K={K} form={_small_m_form(M, K, N)}")
     assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
     print(_linear_case(x, w, b)[0])
 
@@ -334,13 +366,15 @@ def _tie_rows(rng, M, K):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 72, 3072), (5, 72, 3072), (12, 200, 3072), (16, 200, 3072),
+@pytest.mark.parametrize("M,N,K", [(1, 72, 3072), (5, 72, 3072), (13, 18432, 1024),
+                                   (32, 18432, 1024), (12, 200, 3072), (16, 200, 3072),
                                    (20, 200, 3072), (30, 200, 3072), (9, 200, 4112)])
 def test_linear_small_m_rounding_ties(M, N, K):
-    """The fused small-M kernel's on-chip quantisation on rows full of exact
-    rounding ties and on rows with subnormal scales, in each way it holds the
-    rows (one, two, three per wave; K > 3072: read twice): codes and scales
-    bit-exact against the oracle (which rounds fl32(x / s) half to even)."""
+    """The fused small-M kernels' on-chip quantisation on rows full of exact
+    rounding ties and on rows with subnormal scales, in each way they hold the
+    rows (row modes: one, two, three per wave; split roles: from registers,
+    K > 3072 read twice): codes and scales bit-exact against the oracle
+    (which rounds fl32(x / s) half to even)."""
     assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
     rng = np.random.default_rng(M * 101 + K)
     x = _tie_rows(rng, M, K)
