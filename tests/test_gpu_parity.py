@@ -298,22 +298,28 @@ def _small_m_form(M, K, N, cus=256):
     the quantiser waves H (one per row up to 4 rows, else a multiple of 4 that
     fits beside G in 16 waves, at most M); the split kernel for K > 3072 or
     above 8 rows with at most three rows per quantiser, the row modes
-    otherwise. Returns (kernel, detail)."""
+    otherwise. Split: the weight stream whole or refilled (more windows than
+    24, 16 or 12 for 1-2, 3 or 4 token blocks), and the quantisers' rows
+    staged in LDS (when 8 TB slots of 256 ceil(K/128) + 32 bytes fit in
+    159 KiB), in registers, or read twice (K > 3072)."""
     G = min(12, max(4, -(-(-(-N // 8)) // cus)))
     H = M if M <= 4 else min(M, 4 * min(-(-M // 4), (16 - G) // 4))
     TB = -(-M // 8)
     if K > 3072 or (M > 8 and -(-M // H) <= 3):
         depth = {1: 24, 2: 24, 3: 16, 4: 12}[TB]
-        return "split", ("long rows" if K > 3072 else
-                         "refill" if K > 128 * depth else "whole"), TB
+        stream = "refill" if K > 128 * depth else "whole"
+        nwin = -(-K // 128)
+        rows = ("two-pass" if K > 3072 else
+                "staged" if 8 * TB * (256 * nwin + 32) <= 159 * 1024 else "registers")
+        return "split", stream, rows, TB
     W = 12 if TB >= 2 else G
     return "rows", ("one" if M <= W and TB == 1 else "three" if TB == 4 else "two"), TB
 
 
 _WORK_SPLITS = [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040), (12, 18432, 3072),
                 (16, 200, 3072), (3, 72, 4112), (6, 70, 3088), (10, 72, 5136), (13, 18432, 3072),
-                (17, 70, 1040), (20, 200, 3072), (20, 18432, 2048), (25, 200, 3072), (28, 70, 1040),
-                (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)]
+                (17, 70, 1040), (20, 200, 3072), (20, 18432, 2048), (25, 200, 3072), (26, 70, 2048),
+                (28, 70, 1040), (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)]
 
 
 def test_small_m_work_splits_cover_every_form():
@@ -321,9 +327,10 @@ def test_small_m_work_splits_cover_every_form():
     forms = {_small_m_form(M, K, N) for (M, N, K) in _WORK_SPLITS}
     want = {("rows", "one", 1), ("rows", "two", 1), ("rows", "two", 2), ("rows", "two", 3),
             ("rows", "three", 4)}
-    want |= {("split", "long rows", tb) for tb in (1, 2, 3, 4)}
-    want |= {("split", "whole", tb) for tb in (2, 3, 4)}
-    want |= {("split", "refill", tb) for tb in (3, 4)}
+    want |= {("split", "refill", "two-pass", tb) for tb in (1, 2, 3, 4)}
+    want |= {("split", "whole", "staged", tb) for tb in (2, 3, 4)}
+    want |= {("split", "refill", "staged", tb) for tb in (3, 4)}
+    want |= {("split", "refill", "registers", 4)}
     assert want <= forms, want - forms
 
 
@@ -333,9 +340,9 @@ def test_linear_small_m_work_splits(M, N, K):
     each wave holds one, two or three rows in registers across its first
     weight requests (W = 4 waves for N = 33, 70, 72 and 200 and 9 for
     N = 18432 up to M = 8, 12 from M = 9 on); split roles, where quantiser
-    waves without weight rows quantise rows held in registers (K <= 3072)
-    or read twice from memory (longer rows) while the weight waves stream,
-    with all of a row group's windows in flight or refilled as consumed."""
+    waves without weight rows quantise rows staged in LDS, held in
+    registers or read twice from memory while the weight waves stream, with
+    all of a row group's windows in flight or refilled as consumed."""
     rng = np.random.default_rng(M * 31 + N + K)
     x = random_bf16(rng, (M, K))
     w = random_bf16(rng, (N, K), 0.02)

@@ -24,16 +24,18 @@
 //    (measured at M = 16 on 3072 -> 18432: 16.1 us with every window first,
 //    15.0 us with kD0 = 8). All of a CU's rows are in flight at once, one
 //    load latency for the lot.
-//  * split roles: H "quantiser waves" own no weight rows; they request their
-//    first two rows before any weight is requested (a workgroup barrier
-//    orders them), then quantise their rows two in flight, from registers
-//    (K <= 3072) or in two passes from memory (longer rows). The weight waves
-//    request their windows at once and wait at a second barrier. Faster for
-//    long rows (whose row-mode form quantised everything before the first
-//    weight request) and where each quantiser fetches at most three rows
-//    (small N leaves room for up to twelve quantisers); slower where
-//    quantisers fetch rows behind the weight stream (17 to 32 rows on
-//    3072 -> 18432: 15.5 / 21.5 us in row modes, 20.0 / 27.5 us split).
+//  * split roles: H "quantiser waves" own no weight rows. Before any weight
+//    is requested (a workgroup barrier orders them) they request all their
+//    rows into LDS as bf16 by LDS-DMA (buffer_load ... lds) and quantise them
+//    in place; where the LDS slots do not fit, they hold two rows in
+//    registers at a time, and rows longer than 3072 are read twice from
+//    memory. The weight waves request their windows at once and wait at a
+//    second barrier. Faster for long rows (whose row-mode form quantised
+//    everything before the first weight request) and where each quantiser
+//    has at most three rows (small N leaves room for up to twelve
+//    quantisers); slower where four quantisers carry many rows, whose VALU
+//    time then serialises (17 / 32 rows on 3072 -> 18432: 15.5 / 21.5 us
+//    in row modes, 20.0 / 27.5 us split).
 // Streaming, in both: a weight wave requests up to 24 windows at once (one
 // buffer_load_dwordx4 per window: lane l reads row l%8, 16-byte chunk l/8,
 // so every instruction fetches 8 whole 128-byte lines). Each window is one
@@ -85,6 +87,14 @@ constexpr int windows_in_flight(int TB) { return TB >= 4 ? 12 : TB >= 3 ? 16 : 2
 // modulo 256 after the padding (or 32 itself), those 16 chunks fall into 16
 // distinct 16-byte bank groups.
 __host__ __device__ inline int xs_stride(int64_t K) { return (int)((K + 127) / 128) * 128 + 32; }
+
+// Split kernel, how the quantiser waves hold their rows: kRegs, two rows in
+// registers; kStaged, every row in LDS as bf16 (slot stride staged_stride,
+// the int8 codes written over the slot's first K bytes); kTwoPass, rows
+// longer than kRegRowK read twice from memory.
+constexpr int kRegs = 0, kStaged = 1, kTwoPass = 2;
+__host__ __device__ inline int staged_stride(int64_t K) { return (int)((K + 127) / 128) * 256 + 32; }
+constexpr size_t kMaxLds = 160 * 1024 - 1024;   // dynamic LDS a workgroup may take (static: sa_lds)
 
 
 // Quantises the row chunks held in v (chunk lane + 64*u of the row, u < Q)
@@ -320,9 +330,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
 
 // Workgroup: H quantiser waves (0..H-1), then G weight waves. TB: blocks of
 // 8 tokens (1 to 4). REFILL: more windows than windows_in_flight(TB), which
-// are refilled as they are consumed. LONG_ROWS: K > kRegRowK, rows
-// quantised in two passes from memory.
-template <bool HAS_BIAS, int TB, bool REFILL, bool LONG_ROWS, bool F16>
+// are refilled as they are consumed. QMODE: how the quantisers hold their
+// rows (kRegs, kStaged, kTwoPass).
+template <bool HAS_BIAS, int TB, bool REFILL, int QMODE, bool F16>
 __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
     float* __restrict__ sa_out, int vec_flags, int G, int H) {
@@ -334,8 +344,8 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = (int)a.M;
   const int64_t K = a.K, N = a.N;
-  const int ldxs = xs_stride(K);
   const int nwin = (int)((K + 127) / 128);
+  const int ldxs = QMODE == kStaged ? staged_stride(K) : xs_stride(K);
   const uint32_t nchunks = (uint32_t)(K >> 3);
   const bool quantiser = wave < H;
   // weight wave wave-H owns weight rows n_base .. n_base+7
@@ -375,7 +385,36 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
     // only meets weights that read as zero. Token rows >= M give unused
     // columns.
     const int nr = wave < M ? (M - wave + H - 1) / H : 0;
-    if constexpr (!LONG_ROWS) {
+    if constexpr (QMODE == kStaged) {
+      // every row of this wave into its LDS slot as bf16 (LDS-DMA: lane l
+      // of an instruction writes the 16 bytes at LDS base + 16*l), all
+      // requested before any weight window
+      const int row_bytes = (int)K * 2;
+      for (int j = 0; j < nr; ++j) {
+        const int m = wave + H * j;
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(m);
+        for (int c = 0; c < row_bytes; c += 1024)
+          if (c + 16 * lane < row_bytes)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xs + m * ldxs + c, 16, (uint32_t)(c + 16 * lane), 0,
+                                                     0, 0);
+      }
+      lds_barrier();
+      wait_vmcnt<0>();
+      // each row read back whole before its int8 codes overwrite its first K
+      // bytes in place
+      for (int j = 0; j < nr; ++j) {
+        const int m = wave + H * j;
+        uint4 v[kQ];
+#pragma unroll
+        for (int u = 0; u < kQ; ++u) {
+          const uint32_t idx = lane + 64 * u;
+          v[u] = idx < nchunks ? *reinterpret_cast<const uint4*>(xs + m * ldxs + 16 * idx)
+                               : make_uint4(0u, 0u, 0u, 0u);
+        }
+        const float s0 = quantise_regs<F16>(v, nchunks, lane, xs + m * ldxs, nullptr, false);
+        if (lane == 0) sa_lds[m] = s0;
+      }
+    } else if constexpr (QMODE == kRegs) {
       uint4 va[kQ], vb[kQ];
       load_row(va, wave);
       load_row(vb, wave + H);
@@ -539,12 +578,17 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   // otherwise (see the header).
   if (a.K > kRegRowK || (a.M > 8 && (a.M + H - 1) / H <= 3)) {
     const dim3 grid(g.blocks), block(64 * (G + H));
-#define W8A8_SMALL_M(REFILL, LONG_ROWS)                                                             \
-  hipLaunchKernelGGL((small_m_split_kernel<HAS_BIAS, TB, REFILL, LONG_ROWS, F16>), grid, block, lds, \
+#define W8A8_SMALL_M(REFILL, QMODE, LDS)                                                         \
+  hipLaunchKernelGGL((small_m_split_kernel<HAS_BIAS, TB, REFILL, QMODE, F16>), grid, block, LDS, \
                      stream, x, ldx, a, xq_out, a_scale_out, vf, G, H)
-    if (a.K > kRegRowK) W8A8_SMALL_M(true, true);
-    else if (a.K > 128 * windows_in_flight(TB)) W8A8_SMALL_M(true, false);
-    else W8A8_SMALL_M(false, false);
+    const size_t staged_lds = (size_t)(8 * TB) * (size_t)staged_stride(a.K);
+    const bool refill = a.K > 128 * windows_in_flight(TB);
+    if (a.K > kRegRowK) W8A8_SMALL_M(true, kTwoPass, lds);
+    else if (staged_lds <= kMaxLds) {
+      if (refill) W8A8_SMALL_M(true, kStaged, staged_lds);
+      else W8A8_SMALL_M(false, kStaged, staged_lds);
+    } else if (refill) W8A8_SMALL_M(true, kRegs, lds);
+    else W8A8_SMALL_M(false, kRegs, lds);
 #undef W8A8_SMALL_M
     return hipGetLastError();
   }
