@@ -319,7 +319,10 @@ def _small_m_form(M, K, N, cus=256):
 _WORK_SPLITS = [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040), (12, 18432, 3072),
                 (16, 200, 3072), (3, 72, 4112), (6, 70, 3088), (10, 72, 5136), (13, 18432, 3072),
                 (17, 70, 1040), (20, 200, 3072), (20, 18432, 2048), (25, 200, 3072), (26, 70, 2048),
-                (28, 70, 1040), (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096)]
+                (28, 70, 1040), (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096),
+                # the largest LDS staging (156.7 of 159 KiB), the next K in registers,
+                # and three token blocks staged at K = 3072 (148 KiB)
+                (26, 70, 2432), (26, 70, 2448), (24, 70, 3072)]
 
 
 def test_small_m_work_splits_cover_every_form():
