@@ -84,14 +84,19 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None):
     exp = oracle.linear(x_bits, wq_e, sw_e, bias_bits, F16)
     wq, sw = w8.quantize_weights(dev_f16(w_bits))
     if ldx is not None and ldx != K:
-        xpad = np.zeros((M, ldx), np.uint16)
+        # the padding holds 32768.0: read into any row's amax, it would
+        # change that row's scale and every code
+        xpad = np.full((M, ldx), 0x7800, np.uint16)
         xpad[:, :K] = x_bits
         xd = dev_f16(xpad)[:, :K]
     else:
         xd = dev_f16(x_bits)
     bd = None if bias_bits is None else dev_f16(bias_bits)
+    out_full = None
     if ldo is not None and ldo != N:
-        out = torch.empty((M, ldo), dtype=torch.float16, device="cuda")[:, :N]
+        # a sentinel in the output's padding columns, checked after the call
+        out_full = dev_f16(np.full((M, ldo), 0x1234, np.uint16))
+        out = out_full[:, :N]
     else:
         out = torch.empty((M, N), dtype=torch.float16, device="cuda")
     acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
@@ -105,6 +110,8 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None):
     assert_equal(host(xq_d), exp["xq"], "xq")
     assert_equal(host(acc), exp["acc"], "acc")
     stats = assert_bf16_close(host_bits(out), exp["y"])
+    if out_full is not None:
+        assert (host_bits(out_full)[:, N:] == 0x1234).all(), "output padding written"
     out2 = w8.scaled_mm(dev(exp["xq"]), dev(exp["s_a"]), wq, sw, bd, dtype=torch.float16)
     torch.cuda.synchronize()
     assert out2.dtype == torch.float16
@@ -137,13 +144,15 @@ def test_f16_linear_full_size(M, N, K):
     print(_linear_case(x, w, b)[0])
 
 
-def test_f16_linear_strided_x_and_out():
-    rng = np.random.default_rng(22)
-    for M in (5, 40):
-        x = random_f16(rng, (M, 256))
-        w = random_f16(rng, (72, 256), 0.02)
-        announce(f"f16 linear strided M={M}")
-        _linear_case(x, w, None, ldx=264, ldo=75)
+@pytest.mark.parametrize("M,K,ldx", [(5, 256, 264), (40, 256, 264), (12, 256, 264), (3, 3088, 3096)])
+def test_f16_linear_strided_x_and_out(M, K, ldx):
+    """As the bf16 strided test: small-M row modes, the split kernel's staged
+    and two-pass rows, the GEMM path."""
+    rng = np.random.default_rng(22 + M)
+    x = random_f16(rng, (M, K))
+    w = random_f16(rng, (72, K), 0.02)
+    announce(f"f16 linear strided M={M} K={K} ldx={ldx}")
+    _linear_case(x, w, None, ldx=ldx, ldo=75)
 
 
 def test_f16_overflow_and_subnormal_outputs():

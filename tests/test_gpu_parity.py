@@ -118,14 +118,18 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None, check_ws=True):
 
     wq, sw = w8.quantize_weights(dev_bf16(w_bits))
     if ldx is not None and ldx != K:
-        xpad = np.zeros((M, ldx), np.uint16)
+        # the padding holds 65536.0: read into any row's amax, it would
+        # change that row's scale and every code
+        xpad = np.full((M, ldx), 0x4780, np.uint16)
         xpad[:, :K] = x_bits
         xd = dev_bf16(xpad)[:, :K]
     else:
         xd = dev_bf16(x_bits)
     bd = None if bias_bits is None else dev_bf16(bias_bits)
+    out_full = None
     if ldo is not None and ldo != N:
-        out_full = torch.empty((M, ldo), dtype=torch.bfloat16, device="cuda")
+        # a sentinel in the output's padding columns, checked after the call
+        out_full = dev_bf16(np.full((M, ldo), 0x1234, np.uint16))
         out = out_full[:, :N]
     else:
         out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
@@ -142,6 +146,8 @@ def _linear_case(x_bits, w_bits, bias_bits, ldx=None, ldo=None, check_ws=True):
         assert_equal(host(xq_d), exp["xq"], "xq")
     assert_equal(host(acc), exp["acc"], "acc")
     stats = assert_bf16_close(host_bits(out), exp["y"])
+    if out_full is not None:
+        assert (host_bits(out_full)[:, N:] == 0x1234).all(), "output padding written"
 
     # the second op alone on the oracle's quantised activations
     if M > 0:
@@ -197,13 +203,17 @@ def test_linear_modulation_full_size(m):
     print(m, stats)
 
 
-def test_linear_strided_x_and_out():
-    rng = np.random.default_rng(21)
-    for M in (5, 40):
-        x = random_bf16(rng, (M, 256))
-        w = random_bf16(rng, (72, 256), 0.02)
-        announce(f"linear strided M={M}")
-        _linear_case(x, w, None, ldx=264, ldo=75)
+@pytest.mark.parametrize("M,K,ldx", [(5, 256, 264), (40, 256, 264), (12, 256, 264), (20, 256, 264),
+                                     (3, 3088, 3096)])
+def test_linear_strided_x_and_out(M, K, ldx):
+    """Row strides of x and out that differ from K and N, on the small-M row
+    modes (M = 5), the split kernel's LDS-staged rows (M = 12, 20) and
+    two-pass long rows (K = 3088), and the GEMM path (M = 40)."""
+    rng = np.random.default_rng(21 + M)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (72, K), 0.02)
+    announce(f"linear strided M={M} K={K} ldx={ldx}")
+    _linear_case(x, w, None, ldx=ldx, ldo=75)
 
 
 def test_small_m_and_gemm_paths_agree_per_row():
