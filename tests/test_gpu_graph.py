@@ -29,8 +29,9 @@ def _gpu():
 
 
 @pytest.mark.parametrize("M,N,K,with_bias", [
-    (1, 18432, 3072, True),      # small-M kernel, one row per wave
-    (32, 4096, 4096, False),     # small-M kernel, four token blocks
+    (1, 18432, 3072, True),      # small-M row modes, one row per wave
+    (12, 200, 3072, True),       # small-M split kernel, rows staged in LDS
+    (32, 4096, 4096, False),     # small-M split kernel, four token blocks, rows read twice
     (300, 700, 1296, True),      # quantisation + GEMM, one pass
     (64, 4096, 4096, True),      # 64x64 tiles, K split in four
     (512, 4096, 4096, False),    # 128x128 tiles, K split in two

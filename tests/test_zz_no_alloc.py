@@ -56,7 +56,7 @@ def _run_pair(M, K, N, with_bias, seed):
     ((512, 4096, 4096, True), (300, 1040, 700, False)),
     # one-pass GEMM, then the fused small-M kernel
     ((1024, 3072, 3072, False), (8, 3072, 1024, True)),
-    # small-M, then a smaller small-M
+    # the small-M split kernel (rows staged in LDS), then its row-mode kernel
     ((16, 3072, 4096, True), (1, 1040, 520, True)),
 ])
 def test_noalloc_matches_linear_on_two_calls(first, second):
