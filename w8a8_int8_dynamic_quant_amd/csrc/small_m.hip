@@ -375,10 +375,11 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
     for (int u = 0; u < kQ; ++u) v[u] = load16(rx, (uint32_t)(lane + 64 * u) * 16u);
   };
 
-  // The quantiser waves request their first two rows before any weight
-  // window is requested (the first barrier orders them): queued behind a
-  // CU's weight stream, they would arrive only as it drains. The two roles
-  // run apart between the two barriers; every wave passes both.
+  // The quantiser waves request their rows (all of them when staged, the
+  // first two when held in registers) before any weight window is requested
+  // (the first barrier orders them): queued behind a CU's weight stream,
+  // they would arrive only as it drains. The two roles run apart between
+  // the two barriers; every wave passes both.
   if (quantiser) {
     // ---- 1. quantisation into LDS: rows wave, wave + H, ... ----
     // The K tail of each LDS row up to whole windows is never written: it
