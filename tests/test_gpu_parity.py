@@ -311,7 +311,8 @@ def _small_m_form(M, K, N, cus=256):
     otherwise. Split: the weight stream whole or refilled (more windows than
     24, 16 or 12 for 1-2, 3 or 4 token blocks), and the quantisers' rows
     staged in LDS (when 8 TB slots of 256 ceil(K/128) + 32 bytes fit in
-    159 KiB), in registers, or read twice (K > 3072)."""
+    159 KiB; above K = 3072 quantised in two passes over LDS), else in
+    registers (K <= 3072) or read twice from memory."""
     G = min(12, max(4, -(-(-(-N // 8)) // cus)))
     H = M if M <= 4 else min(M, 4 * min(-(-M // 4), (16 - G) // 4))
     TB = -(-M // 8)
@@ -319,8 +320,10 @@ def _small_m_form(M, K, N, cus=256):
         depth = {1: 24, 2: 24, 3: 16, 4: 12}[TB]
         stream = "refill" if K > 128 * depth else "whole"
         nwin = -(-K // 128)
-        rows = ("two-pass" if K > 3072 else
-                "staged" if 8 * TB * (256 * nwin + 32) <= 159 * 1024 else "registers")
+        if 8 * TB * (256 * nwin + 32) <= 159 * 1024:
+            rows = "staged" if K <= 3072 else "staged long"
+        else:
+            rows = "two-pass" if K > 3072 else "registers"
         return "split", stream, rows, TB
     W = 12 if TB >= 2 else G
     return "rows", ("one" if M <= W and TB == 1 else "three" if TB == 4 else "two"), TB
@@ -332,7 +335,11 @@ _WORK_SPLITS = [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040), (12,
                 (28, 70, 1040), (32, 18432, 3072), (24, 70, 3088), (32, 33, 4096),
                 # the largest LDS staging (156.7 of 159 KiB), the next K in registers,
                 # and three token blocks staged at K = 3072 (148 KiB)
-                (26, 70, 2432), (26, 70, 2448), (24, 70, 3072)]
+                (26, 70, 2432), (26, 70, 2448), (24, 70, 3072),
+                # long rows staged at the LDS limit (two token blocks, K = 4992;
+                # one, K = 8192), the next K read twice from memory, and three
+                # token blocks read twice
+                (16, 72, 4992), (16, 72, 5008), (8, 72, 8192), (20, 72, 4096)]
 
 
 def test_small_m_work_splits_cover_every_form():
@@ -340,7 +347,8 @@ def test_small_m_work_splits_cover_every_form():
     forms = {_small_m_form(M, K, N) for (M, N, K) in _WORK_SPLITS}
     want = {("rows", "one", 1), ("rows", "two", 1), ("rows", "two", 2), ("rows", "two", 3),
             ("rows", "three", 4)}
-    want |= {("split", "refill", "two-pass", tb) for tb in (1, 2, 3, 4)}
+    want |= {("split", "refill", "two-pass", tb) for tb in (2, 3, 4)}
+    want |= {("split", "refill", "staged long", tb) for tb in (1, 2, 3)}
     want |= {("split", "whole", "staged", tb) for tb in (2, 3, 4)}
     want |= {("split", "refill", "staged", tb) for tb in (3, 4)}
     want |= {("split", "refill", "registers", 4)}
@@ -388,13 +396,14 @@ def _tie_rows(rng, M, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 72, 3072), (5, 72, 3072), (13, 18432, 1024),
                                    (32, 18432, 1024), (12, 200, 3072), (16, 200, 3072),
-                                   (20, 200, 3072), (30, 200, 3072), (9, 200, 4112)])
+                                   (20, 200, 3072), (30, 200, 3072), (9, 200, 4112),
+                                   (17, 72, 4096)])
 def test_linear_small_m_rounding_ties(M, N, K):
     """The fused small-M kernels' on-chip quantisation on rows full of exact
     rounding ties and on rows with subnormal scales, in each way they hold the
-    rows (row modes: one, two, three per wave; split roles: from registers,
-    K > 3072 read twice): codes and scales bit-exact against the oracle
-    (which rounds fl32(x / s) half to even)."""
+    rows (row modes: one, two, three per wave; split roles: staged in LDS,
+    in registers, read twice from memory): codes and scales bit-exact
+    against the oracle (which rounds fl32(x / s) half to even)."""
     assert w8.linear_path(M, K, N) == w8.PATH_SMALL_M
     rng = np.random.default_rng(M * 101 + K)
     x = _tie_rows(rng, M, K)

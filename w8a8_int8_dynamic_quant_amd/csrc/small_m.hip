@@ -28,8 +28,8 @@
 //    is requested (a workgroup barrier orders them) they request all their
 //    rows into LDS as bf16 by LDS-DMA (buffer_load ... lds) and quantise them
 //    in place; where the LDS slots do not fit, they hold two rows in
-//    registers at a time, and rows longer than 3072 are read twice from
-//    memory. The weight waves request their windows at once and wait at a
+//    registers at a time (K <= 3072) or read longer rows twice from memory.
+//    The weight waves request their windows at once and wait at a
 //    second barrier. Faster for long rows (whose row-mode form quantised
 //    everything before the first weight request) and where each quantiser
 //    has at most three rows (small N leaves room for up to twelve
@@ -88,10 +88,11 @@ constexpr int windows_in_flight(int TB) { return TB >= 4 ? 12 : TB >= 3 ? 16 : 2
 // distinct 16-byte bank groups.
 __host__ __device__ inline int xs_stride(int64_t K) { return (int)((K + 127) / 128) * 128 + 32; }
 
-// Split kernel, how the quantiser waves hold their rows: kRegs, two rows in
-// registers; kStaged, every row in LDS as bf16 (slot stride staged_stride,
-// the int8 codes written over the slot's first K bytes); kTwoPass, rows
-// longer than kRegRowK read twice from memory.
+// Split kernel, how the quantiser waves hold their rows: kStaged, every row
+// in LDS as bf16 (slot stride staged_stride, the int8 codes written over the
+// slot's first K bytes), wherever 8 TB slots fit; otherwise kRegs, two rows
+// in registers (K <= kRegRowK), or kTwoPass, longer rows read twice from
+// memory.
 constexpr int kRegs = 0, kStaged = 1, kTwoPass = 2;
 __host__ __device__ inline int staged_stride(int64_t K) { return (int)((K + 127) / 128) * 256 + 32; }
 constexpr size_t kMaxLds = 160 * 1024 - 1024;   // dynamic LDS a workgroup may take (static: sa_lds)
@@ -328,6 +329,47 @@ __global__ __launch_bounds__(64 * kMaxWaves) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// A row of more than 64*kQ chunks staged in LDS as bf16 (row): an amax pass,
+// then a quantise pass that writes the int8 codes over the row's first K
+// bytes. Codes of chunk batch b land on the bf16 bytes of chunks below half
+// of the batch's first chunk, all read in earlier batches or earlier in this
+// one (a wave's LDS accesses complete in order).
+template <bool F16>
+__device__ __forceinline__ float quantise_lds_long(int8_t* row, uint32_t nchunks, int lane) {
+  constexpr int U = 8;
+  uint32_t amax = 0;
+  for (uint32_t base = 0; base < nchunks; base += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + lane + 64 * u;
+      w[u] = idx < nchunks ? *reinterpret_cast<const uint4*>(row + 16 * idx) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) amax = absmax_bits8(w[u], amax);
+  }
+  amax = wave_max_u32(amax);
+  const float s = row_scale<F16>(amax);
+  const bool zero = (amax == 0);
+  const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;
+  const float r = (zero || exact_div) ? 0.0f : 1.0f / s;
+  for (uint32_t base = 0; base < nchunks; base += 64 * U) {
+    uint4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + lane + 64 * u;
+      w[u] = idx < nchunks ? *reinterpret_cast<const uint4*>(row + 16 * idx) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + lane + 64 * u;
+      const uint2 q = quant8<F16>(w[u], s, r, zero, exact_div);
+      if (idx < nchunks) *reinterpret_cast<uint2*>(row + 8 * idx) = q;
+    }
+  }
+  return s;
+}
+
 // Workgroup: H quantiser waves (0..H-1), then G weight waves. TB: blocks of
 // 8 tokens (1 to 4). REFILL: more windows than windows_in_flight(TB), which
 // are refilled as they are consumed. QMODE: how the quantisers hold their
@@ -401,18 +443,23 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
       }
       lds_barrier();
       wait_vmcnt<0>();
-      // each row read back whole before its int8 codes overwrite its first K
-      // bytes in place
+      // each row read back whole (up to 64*kQ chunks; longer rows in two
+      // passes over LDS) before its int8 codes overwrite its first K bytes
       for (int j = 0; j < nr; ++j) {
         const int m = wave + H * j;
-        uint4 v[kQ];
+        float s0;
+        if (nchunks <= 64u * kQ) {
+          uint4 v[kQ];
 #pragma unroll
-        for (int u = 0; u < kQ; ++u) {
-          const uint32_t idx = lane + 64 * u;
-          v[u] = idx < nchunks ? *reinterpret_cast<const uint4*>(xs + m * ldxs + 16 * idx)
-                               : make_uint4(0u, 0u, 0u, 0u);
+          for (int u = 0; u < kQ; ++u) {
+            const uint32_t idx = lane + 64 * u;
+            v[u] = idx < nchunks ? *reinterpret_cast<const uint4*>(xs + m * ldxs + 16 * idx)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+          }
+          s0 = quantise_regs<F16>(v, nchunks, lane, xs + m * ldxs, nullptr, false);
+        } else {
+          s0 = quantise_lds_long<F16>(xs + m * ldxs, nchunks, lane);
         }
-        const float s0 = quantise_regs<F16>(v, nchunks, lane, xs + m * ldxs, nullptr, false);
         if (lane == 0) sa_lds[m] = s0;
       }
     } else if constexpr (QMODE == kRegs) {
@@ -584,12 +631,16 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
                      stream, x, ldx, a, xq_out, a_scale_out, vf, G, H)
     const size_t staged_lds = (size_t)(8 * TB) * (size_t)staged_stride(a.K);
     const bool refill = a.K > 128 * windows_in_flight(TB);
-    if (a.K > kRegRowK) W8A8_SMALL_M(true, kTwoPass, lds);
-    else if (staged_lds <= kMaxLds) {
+    if (staged_lds <= kMaxLds) {
       if (refill) W8A8_SMALL_M(true, kStaged, staged_lds);
       else W8A8_SMALL_M(false, kStaged, staged_lds);
-    } else if (refill) W8A8_SMALL_M(true, kRegs, lds);
-    else W8A8_SMALL_M(false, kRegs, lds);
+    } else if (a.K > kRegRowK) {
+      W8A8_SMALL_M(true, kTwoPass, lds);
+    } else if (refill) {
+      W8A8_SMALL_M(true, kRegs, lds);
+    } else {
+      W8A8_SMALL_M(false, kRegs, lds);
+    }
 #undef W8A8_SMALL_M
     return hipGetLastError();
   }
