@@ -339,7 +339,10 @@ _WORK_SPLITS = [(4, 70, 1040), (5, 70, 1040), (8, 70, 1040), (9, 70, 1040), (12,
                 # long rows staged at the LDS limit (two token blocks, K = 4992;
                 # one, K = 8192), the next K read twice from memory, and three
                 # token blocks read twice
-                (16, 72, 4992), (16, 72, 5008), (8, 72, 8192), (20, 72, 4096)]
+                (16, 72, 4992), (16, 72, 5008), (8, 72, 8192), (20, 72, 4096),
+                # long rows take down to one weight wave per workgroup: two here,
+                # the last workgroup's second one past N
+                (2, 2056, 4112)]
 
 
 def test_small_m_work_splits_cover_every_form():

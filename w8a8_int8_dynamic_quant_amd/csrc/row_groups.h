@@ -40,12 +40,13 @@ struct RowGroupGrid {
 };
 
 // Enough waves per workgroup that one workgroup per CU covers every group
-// (within the bounds); workgroup b owns groups b*waves .. b*waves+waves-1.
-inline RowGroupGrid row_group_grid(int64_t N) {
+// (from min_waves to kMaxWaves); workgroup b owns groups b*waves ..
+// b*waves+waves-1.
+inline RowGroupGrid row_group_grid(int64_t N, int min_waves = kMinWaves) {
   const int64_t groups = (N + 7) / 8;
   const int64_t cus = device_cus();
   int64_t w = (groups + cus - 1) / cus;
-  w = w < kMinWaves ? kMinWaves : (w > kMaxWaves ? kMaxWaves : w);
+  w = w < min_waves ? min_waves : (w > kMaxWaves ? kMaxWaves : w);
   return RowGroupGrid{(int)w, (unsigned)((groups + w - 1) / w)};
 }
 

@@ -625,10 +625,16 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
   // each quantiser wave has at most three rows to fetch; the row-mode kernel
   // otherwise (see the header).
   if (a.K > kRegRowK || (a.M > 8 && (a.M + H - 1) / H <= 3)) {
-    const dim3 grid(g.blocks), block(64 * (G + H));
+    // Rows longer than kRegRowK: down to one weight wave per workgroup, so
+    // that a narrow weight still spreads over every CU (1 x 8192 -> 2048:
+    // 13.8 -> 11.6 us, 12 x 8192 -> 1024: 18.3 -> 16.4 us; with shorter rows
+    // the four-wave floor measured the same or better)
+    const RowGroupGrid gs = a.K > kRegRowK ? row_group_grid(a.N, 1) : g;
+    const int Gs = gs.waves, Hs = a.K > kRegRowK ? quantiser_waves((int)a.M, Gs) : H;
+    const dim3 grid(gs.blocks), block(64 * (Gs + Hs));
 #define W8A8_SMALL_M(REFILL, QMODE, LDS)                                                         \
   hipLaunchKernelGGL((small_m_split_kernel<HAS_BIAS, TB, REFILL, QMODE, F16>), grid, block, LDS, \
-                     stream, x, ldx, a, xq_out, a_scale_out, vf, G, H)
+                     stream, x, ldx, a, xq_out, a_scale_out, vf, Gs, Hs)
     const size_t staged_lds = (size_t)(8 * TB) * (size_t)staged_stride(a.K);
     const bool refill = a.K > 128 * windows_in_flight(TB);
     if (staged_lds <= kMaxLds) {
