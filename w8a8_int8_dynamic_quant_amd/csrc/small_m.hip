@@ -370,14 +370,17 @@ __device__ __forceinline__ float quantise_lds_long(int8_t* row, uint32_t nchunks
   return s;
 }
 
-// Workgroup: H quantiser waves (0..H-1), then G weight waves. TB: blocks of
-// 8 tokens (1 to 4). REFILL: more windows than windows_in_flight(TB), which
-// are refilled as they are consumed. QMODE: how the quantisers hold their
-// rows (kRegs, kStaged, kTwoPass).
+// Workgroup: H quantiser waves (0..H-1), then S x G weight waves: wave
+// H + p G + g streams part p (of S) of the windows of row group g. TB: blocks
+// of 8 tokens (1 to 4). REFILL: a part has more windows than
+// windows_in_flight(TB), which are refilled as they are consumed. QMODE: how
+// the quantisers hold their rows (kRegs, kStaged, kTwoPass). With S > 1 the
+// parts' int32 sums meet in LDS after the quantised rows (S x G x TB KiB,
+// then G counters) and the last part to finish runs the epilogue.
 template <bool HAS_BIAS, int TB, bool REFILL, int QMODE, bool F16>
 __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, GemmArgs a, int8_t* __restrict__ xq_out,
-    float* __restrict__ sa_out, int vec_flags, int G, int H) {
+    float* __restrict__ sa_out, int vec_flags, int G, int H, int S) {
   extern __shared__ __attribute__((aligned(16))) int8_t xs[];
   __shared__ float sa_lds[8 * TB];
 
@@ -390,9 +393,13 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
   const int ldxs = QMODE == kStaged ? staged_stride(K) : xs_stride(K);
   const uint32_t nchunks = (uint32_t)(K >> 3);
   const bool quantiser = wave < H;
-  // weight wave wave-H owns weight rows n_base .. n_base+7
-  const int64_t n_base = ((int64_t)blockIdx.x * G + (quantiser ? 0 : wave - H)) * 8;
+  // a weight wave streams windows wlo .. whi-1 of weight rows n_base .. n_base+7
+  const int ww = quantiser ? 0 : wave - H;
+  const int grp = ww % G, part = ww / G;
+  const int64_t n_base = ((int64_t)blockIdx.x * G + grp) * 8;
   const int rows_valid = quantiser ? 0 : (int)max<int64_t>(0, min<int64_t>(8, N - n_base));
+  const int nwp = (nwin + S - 1) / S;
+  const int wlo = part * nwp, whi = min(nwin, wlo + nwp);
 
   // weight windows: lane l reads row l%8, 16-byte chunk l/8 of window w
   const __amdgpu_buffer_rsrc_t rw =
@@ -400,7 +407,8 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
   const int chunk = lane >> 3;
   const uint32_t lane_off = (uint32_t)(lane & 7) * (uint32_t)K + 16u * chunk;
   auto wload = [&](int w) -> v4i {
-    const bool in = 128 * w + 16 * chunk < K;          // chunks past K read as zero
+    // chunks past K and windows of the other parts read as zero
+    const bool in = w < whi && 128 * w + 16 * chunk < K;
     // non-temporal: the weight is streamed once; without the hint the loads
     // allocate in caches that a preceding write-heavy kernel left dirty, and
     // the stream waits on their write-back (measured: 21 against 14 us for
@@ -510,11 +518,14 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
   // epilogue scale and bias (row n_base + lane % 8)
   float sw1, bb1;
   load_row_scale<HAS_BIAS, F16>(a.w_scale, a.bias, n_base, rows_valid, lane, sw1, bb1);
+  int8_t* const parts_lds = xs + 8 * TB * ldxs;
+  uint32_t* const done = reinterpret_cast<uint32_t*>(parts_lds + S * G * TB * 1024);
+  if (S > 1 && wave == H && lane < G) done[lane] = 0u;
   lds_barrier();
   v4i buf[kD];
   if (rows_valid > 0) {
 #pragma unroll
-    for (int d = 0; d < kD; ++d) buf[d] = wload(d);
+    for (int d = 0; d < kD; ++d) buf[d] = wload(wlo + d);
     __builtin_amdgcn_sched_barrier(0);     // all requests out before the barrier
   }
   lds_barrier();
@@ -538,20 +549,40 @@ __global__ __launch_bounds__(64 * kMaxSplitWaves) void small_m_split_kernel(
   if constexpr (!REFILL) {
 #pragma unroll
     for (int d = 0; d < kD; ++d) {
-      window(d, buf[d]);
+      window(wlo + d, buf[d]);
       __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
     }
   } else {
-    for (int base = 0; base < nwin; base += kD) {
+    for (int base = 0; base < nwp; base += kD) {
 #pragma unroll
       for (int d = 0; d < kD; ++d) {
-        window(base + d, buf[d]);
-        buf[d] = wload(base + d + kD);
+        window(wlo + base + d, buf[d]);
+        buf[d] = wload(wlo + base + d + kD);
         __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, TB, 0);
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
+    }
+  }
+  if (S > 1) {
+    // this part's sums into LDS; the last part of the group to arrive adds
+    // the others' (int32, exact in any order) and runs the epilogue. The
+    // counter's release orders the wave's stores before it, its acquire the
+    // reads after it.
+    v4i* const mine = reinterpret_cast<v4i*>(parts_lds) + (grp * S + part) * TB * 64;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) mine[t * 64 + lane] = acc[t];
+    uint32_t before = 0u;
+    if (lane == 0)
+      before = __hip_atomic_fetch_add(done + grp, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    before = __builtin_amdgcn_readfirstlane(before);
+    if (before + 1u < (uint32_t)S) return;
+    for (int p = 0; p < S; ++p) {
+      if (p == part) continue;
+      const v4i* const other = reinterpret_cast<const v4i*>(parts_lds) + (grp * S + p) * TB * 64;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[t] += other[t * 64 + lane];
     }
   }
 
@@ -631,13 +662,19 @@ hipError_t launch_variant(const uint16_t* x, int64_t ldx, const GemmArgs& a, int
     // the four-wave floor measured the same or better)
     const RowGroupGrid gs = a.K > kRegRowK ? row_group_grid(a.N, 1) : g;
     const int Gs = gs.waves, Hs = a.K > kRegRowK ? quantiser_waves((int)a.M, Gs) : H;
-    const dim3 grid(gs.blocks), block(64 * (Gs + Hs));
+    // One token block with more windows than a wave keeps in flight: two
+    // weight waves per row group, each streaming half of K, where the
+    // workgroup has room for them
+    const int nwin = (int)((a.K + 127) / 128);
+    const int S = (TB == 1 && nwin > windows_in_flight(TB) && 2 * Gs + Hs <= kMaxSplitWaves) ? 2 : 1;
+    const size_t parts = S > 1 ? (size_t)(S * Gs * TB * 1024 + 4 * Gs) : 0;
+    const dim3 grid(gs.blocks), block(64 * (S * Gs + Hs));
 #define W8A8_SMALL_M(REFILL, QMODE, LDS)                                                         \
-  hipLaunchKernelGGL((small_m_split_kernel<HAS_BIAS, TB, REFILL, QMODE, F16>), grid, block, LDS, \
-                     stream, x, ldx, a, xq_out, a_scale_out, vf, Gs, Hs)
+  hipLaunchKernelGGL((small_m_split_kernel<HAS_BIAS, TB, REFILL, QMODE, F16>), grid, block,      \
+                     (LDS) + parts, stream, x, ldx, a, xq_out, a_scale_out, vf, Gs, Hs, S)
     const size_t staged_lds = (size_t)(8 * TB) * (size_t)staged_stride(a.K);
-    const bool refill = a.K > 128 * windows_in_flight(TB);
-    if (staged_lds <= kMaxLds) {
+    const bool refill = (nwin + S - 1) / S > windows_in_flight(TB);
+    if (staged_lds + parts <= kMaxLds) {
       if (refill) W8A8_SMALL_M(true, kStaged, staged_lds);
       else W8A8_SMALL_M(false, kStaged, staged_lds);
     } else if (a.K > kRegRowK) {
