@@ -30,7 +30,10 @@
 //    in place; where the LDS slots do not fit, they hold two rows in
 //    registers at a time (K <= 3072) or read longer rows twice from memory.
 //    The weight waves request their windows at once and wait at a
-//    second barrier. Faster for long rows (whose row-mode form quantised
+//    second barrier; with one token block and more windows than a wave
+//    keeps in flight, two weight waves share a row group, each streaming
+//    half of K, and their int32 sums meet in LDS. Faster for long rows
+//    (whose row-mode form quantised
 //    everything before the first weight request) and where each quantiser
 //    has at most three rows (small N leaves room for up to twelve
 //    quantisers); slower where four quantisers carry many rows, whose VALU
