@@ -33,10 +33,10 @@
 //    second barrier; with one token block and more windows than a wave
 //    keeps in flight, two weight waves share a row group, each streaming
 //    half of K, and their int32 sums meet in LDS. Faster for long rows
-//    (whose row-mode form quantised
-//    everything before the first weight request) and where each quantiser
-//    has at most three rows (small N leaves room for up to twelve
-//    quantisers); slower where four quantisers carry many rows, whose VALU
+//    (whose row-mode form quantised everything before the first weight
+//    request) and where each quantiser has at most three rows (small N
+//    leaves room for up to twelve quantisers); slower where four
+//    quantisers carry many rows, whose VALU
 //    time then serialises (17 / 32 rows on 3072 -> 18432: 15.5 / 21.5 us
 //    in row modes, 20.0 / 27.5 us split).
 // Streaming, in both: a weight wave requests up to 24 windows at once (one
