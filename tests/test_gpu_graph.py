@@ -32,6 +32,7 @@ def _gpu():
     (1, 18432, 3072, True),      # small-M row modes, one row per wave
     (12, 200, 3072, True),       # small-M split kernel, rows staged in LDS
     (32, 4096, 4096, False),     # small-M split kernel, four token blocks, rows read twice
+    (1, 8192, 4096, True),       # small-M split kernel, two weight waves per row group
     (300, 700, 1296, True),      # quantisation + GEMM, one pass
     (64, 4096, 4096, True),      # 64x64 tiles, K split in four
     (512, 4096, 4096, False),    # 128x128 tiles, K split in two
