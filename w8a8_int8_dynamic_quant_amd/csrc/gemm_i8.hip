@@ -637,12 +637,19 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
 // constant.
 template <bool HAS_BIAS, bool F16, int FM>
 __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n0, int vec_flags,
-                                        int kps, int8_t* lds0, int8_t* lds1, int8_t* lds2,
-                                        int8_t* lds3, float* lds_sa, float* lds_sw, float* lds_b) {
+                                        int kps, int8_t* ring, float* lds_sa, float* lds_sw,
+                                        float* lds_b) {
   constexpr int BM = 64 * FM, BN = 256, BK = 64, KS = BK / 32;
   constexpr int FN = 2;
-  constexpr int HALF = 256 * BK;             // one panel of a stage: 16 KiB
-  constexpr int LPW = 4;                     // requests per wave per stage (its group's panel)
+  constexpr int HALF = 256 * BK;             // the W panel of a stage: 16 KiB
+  constexpr int LPW = 4;                     // requests per requesting wave per stage
+  // Stages in a ring of NB buffers of SB bytes, the W panel then the xq
+  // panel: four of 32 KiB for whole tiles (three stages in flight ahead of
+  // the one being read); six of 24 KiB for halves, whose xq panel is half
+  // as tall (five ahead: a half's stage holds half the MFMA time of a whole
+  // tile's, so the same load latency needs twice the stages)
+  constexpr int NB = FM == 4 ? 4 : 6;
+  constexpr int SB = HALF + BM * BK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -680,7 +687,11 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   const uint32_t lbase = (uint32_t)(64 * wn + (lane >> 2)) * (uint32_t)K + kc;
   const uint32_t rows16 = 16u * (uint32_t)K;
   const int pan = grp * HALF + wn * (LPW * 1024);   // this wave's LDS bytes within a stage
+  // in halves, group 1's waves 2 and 3 would fill xq rows 128..255, which
+  // the packed stage does not have: they request nothing
+  const bool requests = grp == 0 || 64 * wn < BM;
   auto issue_one = [&](int kt, int8_t* st, int u) {
+    if (!requests) return;
     const uint32_t k0 = (uint32_t)kt * BK;
     uint32_t b = lbase;
     asm volatile("" : "+v"(b));
@@ -735,60 +746,59 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   // Every wave runs the same loop body, read(t) | barrier | compute(t) |
   // barrier, with group 1 one phase behind group 0 (an extra barrier at the
   // start; group 1 skips the barrier after its last compute), so stage t is
-  // read in phases 2t (group 0) and 2t+1 (group 1). Right after
-  // its fragment reads of stage t, each wave requests its panel's part of
-  // stage t+3 into the buffer that stage t-1 left at the end of phase 2t-1
+  // read in phases 2t (group 0) and 2t+1 (group 1). Right after its
+  // fragment reads of stage t, each wave requests its panel's part of stage
+  // t+NB-1 into the buffer that stage t-1 left at the end of phase 2t-1
   // (group 0 the W panel in phase 2t, group 1 the xq panel in phase 2t+1),
   // so the loads go out from the waves that are not issuing MFMAs. Every
-  // read phase sends exactly four requests per wave (past the last stage
-  // they read out of bounds: no memory traffic, zeros into a buffer no stage
-  // reads), so both waits are the constant vmcnt(8): a wave's requests of
-  // stage t+1 have landed by the barrier that ends phase 2t+1.
+  // read phase sends exactly four requests per requesting wave (past the
+  // last stage they read out of bounds: no memory traffic, zeros into a
+  // buffer no stage reads), so both waits are the constant
+  // vmcnt((NB-2)*4): a wave's requests of stage t+1 have landed by the
+  // barrier that ends phase 2t+1.
+  auto buf = [&](int i) { return ring + i * SB; };
 #pragma unroll
-  for (int u = 0; u < LPW; ++u) issue_one(kb, lds0, u);
+  for (int i = 0; i < NB - 1; ++i)
 #pragma unroll
-  for (int u = 0; u < LPW; ++u) issue_one(kb + 1, lds1, u);
-#pragma unroll
-  for (int u = 0; u < LPW; ++u) issue_one(kb + 2, lds2, u);
-  wait_vmcnt_lgkm0<2 * LPW>();
+    for (int u = 0; u < LPW; ++u) issue_one(kb + i, buf(i), u);
+  wait_vmcnt_lgkm0<(NB - 2) * LPW>();
   stage_barrier();
   if (grp == 1) stage_barrier();
-  auto body = [&](int s, int8_t* st, int8_t* nx3) {
+  auto body = [&](int s, int8_t* st, int8_t* nxt) {
     read_frags(st);
 #pragma unroll
-    for (int u = 0; u < LPW; ++u) issue_one(s + 3, nx3, u);
-    wait_vmcnt_lgkm0<2 * LPW>();
+    for (int u = 0; u < LPW; ++u) issue_one(s + NB - 1, nxt, u);
+    wait_vmcnt_lgkm0<(NB - 2) * LPW>();
     stage_barrier();
     compute();
-    wait_vmcnt<2 * LPW>();
+    wait_vmcnt<(NB - 2) * LPW>();
     if (grp == 0 || s + 1 < ke) stage_barrier();
   };
-  // (unrolled by four, so that every access names its buffer)
+  // (unrolled by NB, so that every access names its buffer)
   int s = kb;
-  for (; s + 3 < ke; s += 4) {
-    body(s, lds0, lds3);
-    body(s + 1, lds1, lds0);
-    body(s + 2, lds2, lds1);
-    body(s + 3, lds3, lds2);
+  for (; s + NB - 1 < ke; s += NB) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) body(s + i, buf(i), buf((i + NB - 1) % NB));
   }
-  if (s < ke) body(s, lds0, lds3);
-  if (s + 1 < ke) body(s + 1, lds1, lds0);
-  if (s + 2 < ke) body(s + 2, lds2, lds1);
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i)
+    if (s + i < ke) body(s + i, buf(i), buf((i + NB - 1) % NB));
   // every request of this wave (the last ones out of bounds) has written LDS
   wait_vmcnt<0>();
   __builtin_amdgcn_sched_barrier(0);
 
-  // Staging, 8 KiB per wave (half the sub-tile at a time), in a buffer that
-  // no request still in flight targets. With n = ke - kb stages, the last
-  // requests (of stages n, n+1, n+2, relative to kb) target buffers
-  // (n-4) .. (n-2) mod 4, never (n-1) mod 4, and no stage is read after group
-  // 0's last barrier: group 0 stages in buffer (n-1) mod 4. Group 1 stages
-  // after draining its own requests and group 0's last barrier, by which
-  // group 0's requests of stage n (buffer n mod 4) have landed: buffer n mod 4.
+  // Staging (8 KiB per wave for whole tiles, half the sub-tile at a time; 4
+  // KiB for halves), in a buffer that no request still in flight targets.
+  // With n = ke - kb stages, the last requests (of stages n .. n+NB-2,
+  // relative to kb) target buffers n .. n+NB-2 mod NB, never (n-1) mod NB,
+  // and no stage is read after group 0's last barrier: group 0 stages in
+  // buffer (n-1) mod NB. Group 1 stages after draining its own requests and
+  // group 0's last barrier, by which group 0's requests of stage n (buffer
+  // n mod NB) have landed: buffer n mod NB.
   const int n_st = ke - kb;
-  const int pick = grp == 0 ? ((n_st - 1) & 3) : (n_st & 3);
-  int8_t* const stage_buf = pick == 0 ? lds0 : pick == 1 ? lds1 : pick == 2 ? lds2 : lds3;
-  gemm_pp_epilogue<HAS_BIAS, F16, 2, FM>(a, acc, lds_sa, lds_sw, lds_b, stage_buf + wn * 8192, m0,
+  const int pick = grp == 0 ? ((n_st - 1) % NB + NB) % NB : (n_st % NB + NB) % NB;
+  constexpr int REGION = FM == 4 ? 8192 : 4096;
+  gemm_pp_epilogue<HAS_BIAS, F16, 2, FM>(a, acc, lds_sa, lds_sw, lds_b, buf(pick) + wn * REGION, m0,
                                          n0, rows_x, rows_w, grp, wn, lane, vec_flags);
 }
 
@@ -796,24 +806,20 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
 template <bool HAS_BIAS, bool F16>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
                                                         int vec_flags, int kps, int cpx) {
-  constexpr int HALF = 256 * 64;
-  __shared__ __attribute__((aligned(1024))) int8_t lds0[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds1[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds2[2 * HALF];
-  __shared__ __attribute__((aligned(1024))) int8_t lds3[2 * HALF];
+  // the stage ring: 4 x 32 KiB for whole tiles, 6 x 24 KiB for halves
+  __shared__ __attribute__((aligned(1024))) int8_t ring[6 * 24 * 1024];
   __shared__ __attribute__((aligned(16))) float lds_sa[256];
   __shared__ __attribute__((aligned(16))) float lds_sw[256];
   __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? 256 : 1];
   int tm, tn, half;
   if (!tile_coords_halves(tiles_m, tiles_n, cpx, tm, tn, half)) return;
   if (half < 0) {
-    pp_tile<HAS_BIAS, F16, 4>(a, (int64_t)tm * 256, (int64_t)tn * 256, vec_flags, kps, lds0, lds1,
-                              lds2, lds3, lds_sa, lds_sw, lds_b);
+    pp_tile<HAS_BIAS, F16, 4>(a, (int64_t)tm * 256, (int64_t)tn * 256, vec_flags, kps, ring, lds_sa,
+                              lds_sw, lds_b);
   } else {
     const int64_t m0 = (int64_t)tm * 256 + 128 * half;
     if (m0 < a.M)
-      pp_tile<HAS_BIAS, F16, 2>(a, m0, (int64_t)tn * 256, vec_flags, kps, lds0, lds1, lds2, lds3,
-                                lds_sa, lds_sw, lds_b);
+      pp_tile<HAS_BIAS, F16, 2>(a, m0, (int64_t)tn * 256, vec_flags, kps, ring, lds_sa, lds_sw, lds_b);
   }
 }
 
