@@ -631,25 +631,30 @@ __device__ __forceinline__ void gemm_pp_epilogue(const GemmArgs& a, const v16i (
 //
 // A tile is whole (FM = 4: 256 x 256) or, in the last round of an XCD's
 // tiles, one of two 128-row halves (FM = 2: 128 x 256, each wave a 64 x 64
-// sub-tile, eight MFMAs per stage). A half runs the same loop: group 1's
-// requests for rows 128.. of the xq panel read out of bounds (no memory
-// traffic, zeros into LDS rows nothing reads), so every wait keeps its
-// constant.
+// sub-tile, eight MFMAs per 64-byte slice of K). A half runs the same loop
+// on stages of two slices, so each of its phases holds sixteen MFMAs per
+// wave as a whole tile's does; group 1's waves 2 and 3, whose xq rows
+// (128..) the half lacks, request nothing.
 template <bool HAS_BIAS, bool F16, int FM>
 __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n0, int vec_flags,
                                         int kps, int8_t* ring, float* lds_sa, float* lds_sw,
                                         float* lds_b) {
   constexpr int BM = 64 * FM, BN = 256, BK = 64, KS = BK / 32;
   constexpr int FN = 2;
-  constexpr int HALF = 256 * BK;             // the W panel of a stage: 16 KiB
-  constexpr int LPW = 4;                     // requests per requesting wave per stage
-  // Stages in a ring of NB buffers of SB bytes, the W panel then the xq
-  // panel: four of 32 KiB for whole tiles (three stages in flight ahead of
-  // the one being read); six of 24 KiB for halves, whose xq panel is half
-  // as tall (five ahead: a half's stage holds half the MFMA time of a whole
-  // tile's, so the same load latency needs twice the stages)
-  constexpr int NB = FM == 4 ? 4 : 6;
-  constexpr int SB = HALF + BM * BK;
+  constexpr int HALF = 256 * BK;             // the W panel of a 64-byte slice: 16 KiB
+  constexpr int LPW = 4;                     // requests per requesting wave per slice
+  // A stage is SUB slices of 64 bytes of K, each the W panel then the xq
+  // panel (SUBB bytes), in a ring of NB buffers: whole tiles one slice per
+  // stage in four 32 KiB buffers (three stages in flight ahead of the one
+  // being read); halves, whose xq panel is half as tall, two slices per
+  // stage in three 48 KiB buffers, so that a wave runs sixteen MFMAs per
+  // phase as in a whole tile rather than eight, against the same barriers
+  // and the same share of fragment reads
+  constexpr int SUB = FM == 4 ? 1 : 2;
+  constexpr int NB = FM == 4 ? 4 : 3;
+  constexpr int SUBB = HALF + BM * BK;
+  constexpr int SB = SUB * SUBB;
+  constexpr int KST = KS * SUB;              // MFMA k-steps per stage
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -712,17 +717,21 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   const int fb = frag_row * BK + 16 * (frag_half ^ ((frag_row >> 2) & 3));
   const int w_row0 = 64 * wn * BK, x_row0 = HALF + 32 * FM * grp * BK;
 
-  v4i fw[KS][FN], fx[KS][FM];
+  v4i fw[KST][FN], fx[KST][FM];
   auto read_frags = [&](const int8_t* st) {
     int f = fb;
     asm volatile("" : "+v"(f));
 #pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int8_t* p = st + (f ^ (32 * ks));
+      const int8_t* p = st + sub * SUBB + (f ^ (32 * ks));
 #pragma unroll
-      for (int i = 0; i < FN; ++i) fw[ks][i] = *reinterpret_cast<const v4i*>(p + w_row0 + 32 * BK * i);
+      for (int i = 0; i < FN; ++i)
+        fw[sub * KS + ks][i] = *reinterpret_cast<const v4i*>(p + w_row0 + 32 * BK * i);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) fx[ks][j] = *reinterpret_cast<const v4i*>(p + x_row0 + 32 * BK * j);
+      for (int j = 0; j < FM; ++j)
+        fx[sub * KS + ks][j] = *reinterpret_cast<const v4i*>(p + x_row0 + 32 * BK * j);
     }
   };
   // MFMAs of one stage, back to back at raised priority (a VMEM request in
@@ -730,7 +739,7 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   auto compute = [&]() {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KST; ++ks)
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -739,9 +748,19 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
     __builtin_amdgcn_s_setprio(0);
   };
 
+  // stages of SUB slices (a K slice of the tile's range that lies past
+  // kend reads out of bounds: zeros, which add nothing); this kernel never
+  // splits K, so the range starts at slice 0
   const int nk_all = (int)((K + BK - 1) / BK);
-  const int kb = (int)blockIdx.y * kps;
-  const int ke = min(nk_all, kb + kps);
+  const int kb = 0;
+  const int ke = (nk_all + SUB - 1) / SUB;
+  // a stage's requests: SUB x LPW per requesting wave
+  auto issue_stage = [&](int t, int8_t* st) {
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+      for (int u = 0; u < LPW; ++u) issue_one(SUB * t + sub, st + sub * SUBB, u);
+  };
 
   // Every wave runs the same loop body, read(t) | barrier | compute(t) |
   // barrier, with group 1 one phase behind group 0 (an extra barrier at the
@@ -751,27 +770,24 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
   // t+NB-1 into the buffer that stage t-1 left at the end of phase 2t-1
   // (group 0 the W panel in phase 2t, group 1 the xq panel in phase 2t+1),
   // so the loads go out from the waves that are not issuing MFMAs. Every
-  // read phase sends exactly four requests per requesting wave (past the
+  // read phase sends exactly 4 SUB requests per requesting wave (past the
   // last stage they read out of bounds: no memory traffic, zeros into a
   // buffer no stage reads), so both waits are the constant
-  // vmcnt((NB-2)*4): a wave's requests of stage t+1 have landed by the
-  // barrier that ends phase 2t+1.
+  // vmcnt((NB-2)*4*SUB) = vmcnt(8): a wave's requests of stage t+1 have
+  // landed by the barrier that ends phase 2t+1.
   auto buf = [&](int i) { return ring + i * SB; };
 #pragma unroll
-  for (int i = 0; i < NB - 1; ++i)
-#pragma unroll
-    for (int u = 0; u < LPW; ++u) issue_one(kb + i, buf(i), u);
-  wait_vmcnt_lgkm0<(NB - 2) * LPW>();
+  for (int i = 0; i < NB - 1; ++i) issue_stage(kb + i, buf(i));
+  wait_vmcnt_lgkm0<(NB - 2) * SUB * LPW>();
   stage_barrier();
   if (grp == 1) stage_barrier();
   auto body = [&](int s, int8_t* st, int8_t* nxt) {
     read_frags(st);
-#pragma unroll
-    for (int u = 0; u < LPW; ++u) issue_one(s + NB - 1, nxt, u);
-    wait_vmcnt_lgkm0<(NB - 2) * LPW>();
+    issue_stage(s + NB - 1, nxt);
+    wait_vmcnt_lgkm0<(NB - 2) * SUB * LPW>();
     stage_barrier();
     compute();
-    wait_vmcnt<(NB - 2) * LPW>();
+    wait_vmcnt<(NB - 2) * SUB * LPW>();
     if (grp == 0 || s + 1 < ke) stage_barrier();
   };
   // (unrolled by NB, so that every access names its buffer)
@@ -806,8 +822,8 @@ __device__ __forceinline__ void pp_tile(const GemmArgs& a, int64_t m0, int64_t n
 template <bool HAS_BIAS, bool F16>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs a, int tiles_m, int tiles_n,
                                                         int vec_flags, int kps, int cpx) {
-  // the stage ring: 4 x 32 KiB for whole tiles, 6 x 24 KiB for halves
-  __shared__ __attribute__((aligned(1024))) int8_t ring[6 * 24 * 1024];
+  // the stage ring: 4 x 32 KiB for whole tiles, 3 x 48 KiB for halves
+  __shared__ __attribute__((aligned(1024))) int8_t ring[3 * 48 * 1024];
   __shared__ __attribute__((aligned(16))) float lds_sa[256];
   __shared__ __attribute__((aligned(16))) float lds_sw[256];
   __shared__ __attribute__((aligned(16))) float lds_b[HAS_BIAS ? 256 : 1];
