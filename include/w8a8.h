@@ -34,14 +34,10 @@
  *   inputs, and only enqueues work on `stream` (a hipStream_t passed as
  *   void*; NULL = the default stream). A call returns once the work is
  *   enqueued; the caller keeps every buffer alive until the stream has run it.
- * - Two file-scope device arrays are the exceptions to "no state"; each GPU
- *   the library runs on holds them until the process ends:
- *   - the 256 KiB lookup table of w8a8_gelu_quant_act (bf16 z -> bf16
- *     GELU(z), one table per form). A table-path call rewrites it on the
- *     caller's stream before using it, always with the same values, so calls
- *     on different streams only ever write identical bytes and no call
- *     depends on an earlier one;
- *   - the 64 MiB scratch of w8a8_linear_noalloc (see there).
+ * - One file-scope device array is the exception to "no state": the 64 MiB
+ *   scratch of w8a8_linear_noalloc (see there), which each GPU the library
+ *   runs on holds until the process ends. (The 256 KiB GELU lookup table of
+ *   w8a8_gelu_quant_act is read-only data built into the library.)
  * - Layouts are row-major. bf16 values are passed as uint16_t bit patterns.
  * - Arguments are validated before anything is launched; on an error nothing
  *   is enqueued and an error status is returned (no exceptions, no abort).

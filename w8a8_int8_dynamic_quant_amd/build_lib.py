@@ -2,7 +2,9 @@
 
     python -m w8a8_int8_dynamic_quant_amd.build_lib
 
-Every source under csrc/ is compiled to an object under _build/ and linked
+First the host program csrc/gen_gelu_table.cpp is built with g++ and run: it
+writes _build/gelu_table.inc, the GELU producer's bf16 -> bf16 tables. Then
+every source under csrc/ is compiled to an object under _build/ and linked
 into w8a8_int8_dynamic_quant_amd/libw8a8.so.
 """
 from __future__ import annotations
@@ -34,6 +36,34 @@ HIPCC_FLAGS = [
 ]
 
 
+# The GELU tables are computed with the same fp32 operations as the GPU
+# kernel (gelu_f32.h): no contraction into fused multiply-adds, IEEE
+# division and denormals (no -ffast-math).
+GXX_FLAGS = ["-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
+
+
+def gen_gelu_table(verbose: bool = False, build_dir: str = BUILD) -> str:
+    """Builds and runs the GELU table generator; returns the path of the
+    gelu_table.inc it wrote under build_dir."""
+    gxx = shutil.which("g++")
+    if not gxx:
+        raise RuntimeError("g++ not found: it builds the GELU table generator")
+    os.makedirs(build_dir, exist_ok=True)
+    exe = os.path.join(build_dir, "gen_gelu_table")
+    out = os.path.join(build_dir, "gelu_table.inc")
+    cmd = [gxx, *GXX_FLAGS, "-I", CSRC, os.path.join(CSRC, "gen_gelu_table.cpp"), "-o", exe]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("gen_gelu_table build failed:\n" + r.stdout.decode(errors="replace"))
+    r = subprocess.run([exe, out + ".tmp"], stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("gen_gelu_table failed:\n" + r.stdout.decode(errors="replace"))
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -47,13 +77,14 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    gen_gelu_table(verbose)
     cc = hipcc()
     procs = []
     objs = []
     for src in sources():
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, "-I", BUILD, "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -30,30 +30,21 @@
 //   y = fma(fma(x, rstd, -(mean rstd)), 1 + scale, shift): two roundings
 //   fewer than the literal order, and the rounding of mean rstd is within
 //   the error the mean itself carries (u |mean| rstd).
-//   GELU: (0.5 z) * erfc(-z / sqrt 2), which has no cancellation for z << 0,
-//   with erfc(x) = t exp(-x^2 + P(t)), t = 1 / (1 + x/2), for x = |z| / sqrt 2
-//   (2 - erfc(x) for z > 0): the form of Numerical Recipes' Chebyshev erfc
-//   (section 6.2), P a degree-9 polynomial of our own fit, within 2 fp32 ulps
-//   (gen_erfc_poly.py).
-//   tanh form: with t = sqrt(2/pi) (z + 0.044715 z^3) and e = exp(-2|t|),
-//   z / (1 + e) for t >= 0 and z e / (1 + e) for t < 0 (the same function as
-//   0.5 z (1 + tanh t), without the overflow of exp(-2t) at t << 0).
-//   exp and 1/x are the hardware's v_exp_f32 (2^x) and v_rcp_f32 (each within
-//   about an ulp); an exponent below -64 is raised by 64 and the result scaled
-//   back by 2^-64 at the end, so that results in the subnormal range are kept.
-//   The bf16 rounding is v_cvt_pk_bf16_f32 (nearest even, subnormals kept).
+//   GELU: the fp32 evaluation of gelu_f32.h (erf and tanh forms, IEEE
+//   operations only). The bf16 rounding is v_cvt_pk_bf16_f32 (nearest even,
+//   subnormals kept).
 //
 // GELU on large inputs goes through a table instead: a bf16 input has 65536
 // values, so the whole map z -> bf16(GELU(z)) is 128 KB, which fits in one
-// compute unit's 160 KB of LDS. A small kernel evaluates the map with the
-// fp32 code above (the same bits the per-element kernel produces) into a
-// static device array on the caller's stream; the quantisation kernel then
-// copies it into LDS once per workgroup (one 1024-thread workgroup per
-// compute unit, four rows at a time, four waves to a row) and replaces the ~30 VALU
-// instructions per element of the formula by one LDS lookup, leaving the row
-// stream HBM-bound. Every call rebuilds the table with the same values, so
-// calls on different streams only ever write identical bytes.
-#include "erfc_poly.h"
+// compute unit's 160 KB of LDS. Because gelu_f32.h uses only IEEE operations,
+// the host computes the same bits as this kernel's per-element path, so the
+// map of each form is tabulated at build time (gen_gelu_table.cpp) and built
+// into the library as read-only data; nothing is computed or written for it
+// at run time. The quantisation kernel copies it into LDS once per workgroup
+// (one 1024-thread workgroup per compute unit, four rows at a time, four
+// waves to a row) and replaces the formula's ~45 VALU instructions per element
+// by one LDS lookup, leaving the row stream HBM-bound.
+#include "gelu_f32.h"
 #include "producers.h"
 #include "row_groups.h"
 #include "w8a8_device.h"
@@ -110,40 +101,6 @@ __device__ __forceinline__ uint4 pack8_bf16(const float (&f)[8]) {
   for (int i = 0; i < 4; ++i)
     w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){f[2 * i], f[2 * i + 1]}, v2bf));
   return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-constexpr float kLog2e = 1.44269504088896341f;
-
-// GELU in fp32 without branches. 2^q comes from v_exp_f32; where q < -64 it
-// is taken as 2^(q + 64) and the result scaled back by 2^-64 at the end, so
-// results in the fp32 subnormal range are kept. On the positive side such a
-// term is below 2^-64 and drops out of 1 + e (or 2 - erfc) exactly.
-__device__ __forceinline__ float gelu_erf(float z) {
-#pragma clang fp contract(off)
-  const float x = __builtin_fabsf(z) * 0.707106781186547524f;     // |z| / sqrt 2
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(x, 0.5f, 1.0f));
-  float p = kErfcPoly[kErfcPolyDegree];
-#pragma unroll
-  for (int i = kErfcPolyDegree - 1; i >= 0; --i) p = __builtin_fmaf(p, t, kErfcPoly[i]);
-  const float q = (p - x * x) * kLog2e;
-  const bool shifted = q < -64.0f;
-  const float c = t * __builtin_amdgcn_exp2f(shifted ? q + 64.0f : q);   // erfc(x) (* 2^64)
-  const bool pos = z > 0.0f;
-  const float y = (0.5f * z) * (pos ? 2.0f - (shifted ? 0.0f : c) : c);  // erfc(-x) = 2 - erfc(x)
-  return (shifted && !pos) ? y * 0x1p-64f : y;
-}
-
-__device__ __forceinline__ float gelu_tanh(float z) {
-#pragma clang fp contract(off)
-  const float z3 = (z * z) * z;
-  const float t = 0.797884560802865355f * (z + 0.044715f * z3);   // sqrt(2/pi)
-  const float q = (-2.0f * kLog2e) * __builtin_fabsf(t);
-  const bool shifted = q < -64.0f;
-  const float e = __builtin_amdgcn_exp2f(shifted ? q + 64.0f : q);     // exp(-2|t|) (* 2^64)
-  const float r = __builtin_amdgcn_rcpf(1.0f + (shifted ? 0.0f : e));
-  const bool pos = t >= 0.0f;
-  const float y = (pos ? z : z * e) * r;
-  return (shifted && !pos) ? y * 0x1p-64f : y;
 }
 
 // Adds the WPR per-wave values of this wave's row in part order (the same
@@ -268,7 +225,7 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
       unpack8(v[c], f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        f[i] = OP == kProducerGelu ? gelu_erf(f[i]) : gelu_tanh(f[i]);
+        f[i] = OP == kProducerGelu ? gelu::gelu_erf(f[i]) : gelu::gelu_tanh(f[i]);
         amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(f[i]));
       }
       v[c] = pack8_bf16(f);
@@ -300,20 +257,16 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
   if (lane == 0 && part == 0) a.a_scale[row] = s;
 }
 
-// z -> bf16(GELU(z)) for every bf16 bit pattern z, erf form then tanh form.
-__device__ __attribute__((aligned(16))) uint16_t g_gelu_table[2][65536];
+// z -> bf16(GELU(z)) for every bf16 bit pattern z, erf form then tanh form:
+// read-only data, tabulated on the host at build time with the fp32
+// evaluation of gelu_f32.h (gen_gelu_table.cpp), bit for bit what the
+// per-element kernel computes.
+__device__ __attribute__((aligned(16))) const uint16_t g_gelu_table[2][65536] = {
+#include "gelu_table.inc"
+};
 
 constexpr int kLutWaves = 16;                        // waves per lookup workgroup
 constexpr size_t kLutBytes = 65536 * sizeof(uint16_t);
-
-template <int OP>
-__global__ __launch_bounds__(256) void gelu_table_kernel() {
-  const uint32_t z = blockIdx.x * 256u + threadIdx.x;          // grid 256 x 256
-  const float zf = bf16_to_f32(z);
-  const float y = OP == kProducerGelu ? gelu_erf(zf) : gelu_tanh(zf);
-  g_gelu_table[OP - kProducerGelu][z] =
-      (uint16_t)__builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){y, 0.0f}, v2bf));
-}
 
 // WPR waves per row (wave part p holds chunks lane + 64 (p + WPR c), c < CH),
 // 16 / WPR rows per iteration of the workgroup. Each wave requests its part
@@ -322,22 +275,19 @@ __global__ __launch_bounds__(256) void gelu_table_kernel() {
 // swap by name: a register copy of a row still in flight would wait for it
 // there); the parts of a row exchange their amax through LDS slots,
 // double-buffered by iteration so one barrier per iteration suffices (no wave
-// runs more than one iteration ahead of another). Every wave of a workgroup
-// runs the same number of iterations; a row past M reads zero and stores
-// nothing.
+// runs more than one iteration ahead of another). Iteration k of workgroup b
+// (of G) takes rows k S + g G + b, S = G * 16 / WPR, for its row groups
+// g = 0, 1, ...: a partial last sweep over M then gives every workgroup at
+// most one row fewer than the others, rather than leaving the workgroups
+// past its end idle. Every wave of a workgroup runs the same number of
+// iterations (while its group 0 has a row); a row past M reads zero and
+// stores nothing.
 template <int OP, int CH, int WPR>
 __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(ProducerArgs a) {
   static_assert(WPR == 4 || WPR == 8 || WPR == 16, "waves per row");
   constexpr int RPI = kLutWaves / WPR;               // rows per iteration
   extern __shared__ __attribute__((aligned(16))) uint16_t lut[];
   __shared__ uint32_t part_max[2][kLutWaves];
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(g_gelu_table[OP - kProducerGelu]);
-    uint4* dst = reinterpret_cast<uint4*>(lut);
-    constexpr int kPer = (int)(kLutBytes / 16) / (64 * kLutWaves);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) dst[threadIdx.x + 64 * kLutWaves * i] = src[threadIdx.x + 64 * kLutWaves * i];
-  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = wave % WPR;
@@ -403,11 +353,23 @@ __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(Producer
       if (lane == 0 && part == 0) a.a_scale[row] = s;
     }
   };
-  // iteration k runs while the workgroup's first row of it is below M
-  auto live = [&](int k) { return (int64_t)blockIdx.x * RPI + k * stride < a.M; };
-  int64_t row = (int64_t)blockIdx.x * RPI + wave / WPR;
+  // iteration k runs while the workgroup's row of group 0 is below M
+  auto live = [&](int k) { return (int64_t)blockIdx.x + k * stride < a.M; };
+  int64_t row = (int64_t)blockIdx.x + (int64_t)(wave / WPR) * gridDim.x;
   uint4 b0[CH], b1[CH];
+  // the first row is requested before the table: its HBM latency then
+  // overlaps the table's copy from L2
   load_row(row, b0);
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(g_gelu_table[OP - kProducerGelu]);
+    uint4* dst = reinterpret_cast<uint4*>(lut);
+    constexpr int kPer = (int)(kLutBytes / 16) / (64 * kLutWaves);
+    uint4 t[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) t[i] = src[threadIdx.x + 64 * kLutWaves * i];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) dst[threadIdx.x + 64 * kLutWaves * i] = t[i];
+  }
   __syncthreads();                                  // the table is in LDS
   for (int k = 0; live(k); k += 2, row += 2 * stride) {
     load_row(row + stride, b1);
@@ -420,8 +382,6 @@ __global__ __launch_bounds__(64 * kLutWaves) void gelu_lut_quant_kernel(Producer
 
 template <int OP, int CH, int WPR>
 hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((gelu_table_kernel<OP>), dim3(256), dim3(256), 0, stream);
-  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int RPI = kLutWaves / WPR;
   const int64_t wgs_needed = (a.M + RPI - 1) / RPI;
   const int64_t cus = device_cus();
@@ -431,7 +391,7 @@ hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The table path pays for its table build (65536 evaluations) from about
+// The table path pays for its per-workgroup 128 KB table copy from about
 // 4 M elements on; 4 or 16 waves hold a row, at most 2 chunks per lane
 // (rows up to K = 16384 take it).
 constexpr int64_t kLutMinElements = int64_t(1) << 22;
