@@ -158,7 +158,10 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
 #pragma unroll
   for (int c = 0; c < CH; ++c) v[c] = load16_nt(rx, (uint32_t)(lane + 64 * (part + WPR * c)) * 16u);
   if constexpr (OP == kProducerLayerNorm) {
-    const int64_t g = (valid ? row : 0) / a.rows_per_group;
+    // the row's modulation group: 32-bit division where both fit (the
+    // 64-bit one is a long instruction sequence ahead of these loads)
+    const uint64_t r64 = (uint64_t)(valid ? row : 0), rpg = (uint64_t)a.rows_per_group;
+    const int64_t g = (r64 | rpg) >> 32 ? (int64_t)(r64 / rpg) : (int64_t)((uint32_t)r64 / (uint32_t)rpg);
     const __amdgpu_buffer_rsrc_t rsh = make_rsrc(a.shift + g * a.ld_mod, row_bytes);
     const __amdgpu_buffer_rsrc_t rsc = make_rsrc(a.scale + g * a.ld_mod, row_bytes);
 #pragma unroll
