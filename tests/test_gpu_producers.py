@@ -232,7 +232,7 @@ def test_gelu_full_dit_rows(approximate):
     assert st["n_not_nearest"] <= st["n"] // 1000, st
 
 
-# GELU calls of at least 2^22 elements with K <= 16384 take the table path
+# GELU calls of at least 2^22 elements with K <= 32768 take the table path
 # (the whole bf16 -> bf16 map in LDS); it must give the same bits as the
 # per-element kernel, which smaller calls take.
 LUT_MIN = 1 << 22
@@ -259,10 +259,12 @@ def test_gelu_table_path_every_bf16_value(approximate):
 
 @pytest.mark.parametrize("approximate", ["none", "tanh"])
 @pytest.mark.parametrize("M,K", [(1100, 4112), (262160, 16), (400, 12288), (3001, 1552),
-                                 (520, 8192), (300, 16384)])
+                                 (520, 8192), (300, 16384), (260, 16400), (180, 24576),
+                                 (130, 32768)])
 def test_gelu_table_path_shapes(approximate, M, K):
     """Ragged K (past-K chunks in a lane's last slots), one to eight chunks
-    per lane up to the longest table-path rows (K = 16384), and more rows
+    per lane on four waves per row up to K = 16384 and on eight waves per row
+    beyond it (K = 16400, 24576, 32768), and more rows
     than the grid takes in one pass."""
     assert M * K >= LUT_MIN
     rng = np.random.default_rng(M + K)

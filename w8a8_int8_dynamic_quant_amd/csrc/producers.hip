@@ -395,22 +395,26 @@ hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
 }
 
 // The table path pays for its per-workgroup 128 KB table copy from about
-// 4 M elements on; 4 or 16 waves hold a row, at most 2 chunks per lane
-// (rows up to K = 16384 take it).
+// 4 M elements on; 4 waves hold a row of up to 16384 elements, 8 waves a
+// longer one (up to 32768), at most 8 chunks per lane.
 constexpr int64_t kLutMinElements = int64_t(1) << 22;
-constexpr int64_t kLutMaxChunks = 2048;
+constexpr int64_t kLutMaxChunks = 4096;
 
 template <int OP>
 hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
   // waves per row: at 4352 x 12288, 4 ran in 45 us, 8 in 50 us, 16 in
-  // 57 us (wider rows mean more waves at each barrier)
+  // 57 us (wider rows mean more waves at each barrier); rows of more than
+  // 16384 elements take 8, so that a lane holds at most 8 chunks
   constexpr int W = 4;
   const int64_t per_lane = ((a.K >> 3) + 64 * W - 1) / (64 * W);
   if (per_lane <= 1) return launch_lut<OP, 1, W>(a, stream);
   if (per_lane <= 2) return launch_lut<OP, 2, W>(a, stream);
   if (per_lane <= 4) return launch_lut<OP, 4, W>(a, stream);
   if (per_lane <= 6) return launch_lut<OP, 6, W>(a, stream);
-  return launch_lut<OP, 8, W>(a, stream);
+  if (per_lane <= 8) return launch_lut<OP, 8, W>(a, stream);
+  const int64_t per_lane8 = ((a.K >> 3) + 64 * 8 - 1) / (64 * 8);
+  if (per_lane8 <= 6) return launch_lut<OP, 6, 8>(a, stream);
+  return launch_lut<OP, 8, 8>(a, stream);
 }
 
 template <int OP, int CH, int WPR>
