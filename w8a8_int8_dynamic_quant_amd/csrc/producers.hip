@@ -41,9 +41,10 @@
 // map of each form is tabulated at build time (gen_gelu_table.cpp) and built
 // into the library as read-only data; nothing is computed or written for it
 // at run time. The quantisation kernel copies it into LDS once per workgroup
-// (one 1024-thread workgroup per compute unit, four rows at a time, four
-// waves to a row) and replaces the formula's ~45 VALU instructions per element
-// by one LDS lookup, leaving the row stream HBM-bound.
+// (one 1024-thread workgroup per compute unit, four rows at a time with four
+// waves to a row, or two rows with eight waves for rows of more than 16384
+// elements) and replaces the formula's ~45 VALU instructions per element by
+// one LDS lookup.
 #include "gelu_f32.h"
 #include "producers.h"
 #include "row_groups.h"
