@@ -301,10 +301,11 @@ int w8a8_layernorm_modulate_quant_act(const uint16_t* x, int64_t M, int64_t K, i
 /*
  * GELU, the activation in front of a DiT block's FFN-down linear:
  *   W8A8_GELU_ERF:  y = bf16(z Phi(z)), Phi the standard normal distribution
- *                   function, evaluated as (0.5 z) erfc(-z / sqrt 2);
- *   W8A8_GELU_TANH: y = bf16(0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))),
- *                   evaluated as z / (1 + e) (t >= 0) or z e / (1 + e) (t < 0),
- *                   e = exp(-2|t|), t the tanh argument.
+ *                   function;
+ *   W8A8_GELU_TANH: y = bf16(0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))).
+ *   y is the bf16 nearest to GELU(z) (half to even) as evaluated in double
+ *   precision: the library carries the whole bf16 -> bf16 map of each form,
+ *   computed at build time, and looks every element up.
  *   z [M, ldz] bf16 (read)
  * Limits: K <= 32768 (else W8A8_ERR_UNSUPPORTED); approximate one of the two
  * values (else W8A8_ERR_INVALID_ARG).

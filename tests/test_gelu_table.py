@@ -1,14 +1,16 @@
-"""The GELU producer's build-time tables (csrc/gen_gelu_table.cpp over the
-fp32 evaluation of csrc/gelu_f32.h), CPU only.
+"""The GELU producer's build-time tables (csrc/gen_gelu_table.cpp: GELU in
+double precision, rounded once to the nearest bf16), CPU only.
 
 The generator is the product's own host program: build_lib runs it at build
-time, and the library looks its output up on the GPU (the per-element GPU
-kernel computes the same bits; the GPU tests compare the two paths on every
-finite bf16 input). Here it is built and run on the host, and each of its
-65536-entry tables is checked against the oracle: for every finite bf16 z the
-entry must be a correct bf16 result for the exact GELU(z) within the fp32
-bound the oracle derives (oracle.gelu_err_bound), and at most one entry in a
-thousand may be the other bf16 neighbour of GELU(z)."""
+time, and the library's GELU kernel looks its output up on the GPU (the GPU
+tests compare the kernel's output with these tables on every finite bf16
+input). Here it is built and run on the host, and each of its 65536-entry
+tables is checked against the oracle: for every finite bf16 z the entry must
+be a correct bf16 result for the exact GELU(z) within the bound the oracle
+derives (oracle.gelu_err_bound), and it must be the nearest bf16 to the
+oracle's float64 GELU(z) (two entries of slack for a value within a few
+float64 ulps of a bf16 midpoint, where two float64 evaluations may round
+apart)."""
 import re
 import shutil
 
@@ -39,11 +41,14 @@ def test_every_finite_bf16_within_bound(tables, form, approximate):
     ok = oracle.bf16_within(y, v, oracle.gelu_err_bound(z, approximate))
     assert ok.all(), (z[~ok][:5], y[~ok][:5], v[~ok][:5])
     not_nearest = int(np.count_nonzero(y != oracle.f64_to_bf16_bits(v)))
-    assert not_nearest <= z.size // 1000, not_nearest
+    assert not_nearest <= 2, not_nearest
 
 
-def test_zero_and_signs(tables):
-    # GELU(+-0) = +-0 in both forms; GELU(z) > 0 for z > 0, <= 0 for z < 0
+def test_zero_infinities_and_signs(tables):
+    # GELU(+-0) = +-0 and GELU(+inf) = +inf, GELU(-inf) = -0 (the limits) in
+    # both forms; GELU(z) > 0 for z > 0, <= 0 for z < 0
+    for form in (0, 1):
+        assert tables[form][0x7F80] == 0x7F80 and tables[form][0xFF80] == 0x8000
     z = all_finite_bf16()
     neg = (z & 0x8000) != 0
     for form in (0, 1):

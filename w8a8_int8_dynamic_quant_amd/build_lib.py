@@ -3,7 +3,8 @@
     python -m w8a8_int8_dynamic_quant_amd.build_lib
 
 First the host program csrc/gen_gelu_table.cpp is built with g++ and run: it
-writes _build/gelu_table.inc, the GELU producer's bf16 -> bf16 tables. Then
+writes _build/gelu_table.inc, the GELU producer's bf16 -> bf16 tables
+(GELU in double precision, rounded once to the nearest bf16). Then
 every source under csrc/ is compiled to an object under _build/ and linked
 into w8a8_int8_dynamic_quant_amd/libw8a8.so.
 """
@@ -36,9 +37,8 @@ HIPCC_FLAGS = [
 ]
 
 
-# The GELU tables are computed with the same fp32 operations as the GPU
-# kernel (gelu_f32.h): no contraction into fused multiply-adds, IEEE
-# division and denormals (no -ffast-math).
+# The GELU tables are computed in IEEE double precision (no fast-math, no
+# contraction) and rounded once to bf16.
 GXX_FLAGS = ["-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-Wall"]
 
 
@@ -51,7 +51,7 @@ def gen_gelu_table(verbose: bool = False, build_dir: str = BUILD) -> str:
     os.makedirs(build_dir, exist_ok=True)
     exe = os.path.join(build_dir, "gen_gelu_table")
     out = os.path.join(build_dir, "gelu_table.inc")
-    cmd = [gxx, *GXX_FLAGS, "-I", CSRC, os.path.join(CSRC, "gen_gelu_table.cpp"), "-o", exe]
+    cmd = [gxx, *GXX_FLAGS, os.path.join(CSRC, "gen_gelu_table.cpp"), "-o", exe]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)

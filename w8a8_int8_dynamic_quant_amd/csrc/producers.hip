@@ -12,40 +12,33 @@
 // to even), and, when asked, y itself: what the unfused producer would have
 // written and the quantisation would have read back.
 //
-// Layout and schedule follow the quantisation kernels: one, two or four
-// waves per row (two from K > 1024, four from K > 4096), lane `lane` of wave part p
-// holding the row's 16-byte chunks lane + 64 (p + WPR c), c < CH, all
+// The LayerNorm kernel follows the quantisation kernels: one, two or four
+// waves per row (two from K > 1024, four from K > 4096), lane `lane` of wave
+// part p holding the row's 16-byte chunks lane + 64 (p + WPR c), c < CH, all
 // requested at once (non-temporal: x is read once) and kept in registers
 // through every step, so the row is read from HBM once and written once as
 // int8. Chunks past K read zero through the bounded buffer descriptor and are
-// masked out of the sums and the amax.
+// masked out of the sums and the amax. Its fp32 evaluation (no contraction;
+// correctly rounded division and square root): each lane sums its 8 CH
+// values in order, a DPP reduction adds the lanes (six additions per term;
+// one lane's total is used by every lane) and the WPR wave sums are added in
+// part order: no term passes through more than K / 64 + 16 additions.
+// mean = sum / K, var = (sum of (x - mean)^2) / K (squares accumulated by
+// fused multiply-add), rstd = 1 / sqrt(var + eps),
+// y = fma(fma(x, rstd, -(mean rstd)), 1 + scale, shift): two roundings fewer
+// than the literal order, and the rounding of mean rstd is within the error
+// the mean itself carries (u |mean| rstd). The bf16 rounding is
+// v_cvt_pk_bf16_f32 (nearest even, subnormals kept).
 //
-// fp32 evaluation (no contraction; correctly rounded division and square
-// root):
-//   LayerNorm: each lane sums its 8 CH values in order, a DPP reduction
-//   adds the lanes (six additions per term; one lane's total is used by
-//   every lane) and the WPR wave sums are added in part order: no term
-//   passes through more than K / 64 + 16 additions. mean = sum / K, var = (sum of (x - mean)^2) / K
-//   (squares accumulated by fused multiply-add), rstd = 1 / sqrt(var + eps),
-//   y = fma(fma(x, rstd, -(mean rstd)), 1 + scale, shift): two roundings
-//   fewer than the literal order, and the rounding of mean rstd is within
-//   the error the mean itself carries (u |mean| rstd).
-//   GELU: the fp32 evaluation of gelu_f32.h (erf and tanh forms, IEEE
-//   operations only). The bf16 rounding is v_cvt_pk_bf16_f32 (nearest even,
-//   subnormals kept).
-//
-// GELU on large inputs goes through a table instead: a bf16 input has 65536
-// values, so the whole map z -> bf16(GELU(z)) is 128 KB, which fits in one
-// compute unit's 160 KB of LDS. Because gelu_f32.h uses only IEEE operations,
-// the host computes the same bits as this kernel's per-element path, so the
-// map of each form is tabulated at build time (gen_gelu_table.cpp) and built
-// into the library as read-only data; nothing is computed or written for it
-// at run time. The quantisation kernel copies it into LDS once per workgroup
-// (one 1024-thread workgroup per compute unit, four rows at a time with four
-// waves to a row, or two rows with eight waves for rows of more than 16384
-// elements) and replaces the formula's ~45 VALU instructions per element by
-// one LDS lookup.
-#include "gelu_f32.h"
+// GELU goes through a table: a bf16 input has 65536 values, so the whole map
+// z -> bf16(GELU(z)) is 128 KB, which fits in one compute unit's 160 KB of
+// LDS. The map of each form is computed at build time in double precision
+// and rounded once to the nearest bf16 (gen_gelu_table.cpp), and the library
+// carries it as read-only data; nothing is computed or written for it at run
+// time. The kernel copies it into LDS once per workgroup (one 1024-thread
+// workgroup per compute unit, four rows at a time with four waves to a row,
+// or two rows with eight waves for rows of more than 16384 elements), and
+// each element is one LDS lookup.
 #include "producers.h"
 #include "row_groups.h"
 #include "w8a8_device.h"
@@ -136,8 +129,11 @@ __device__ __forceinline__ uint32_t row_max_parts(uint32_t v, uint32_t* slot, in
   }
 }
 
+// The modulated LayerNorm fused with the quantisation (OP is always
+// kProducerLayerNorm: GELU takes the table kernel below).
 template <int OP, int CH, int WPR>
 __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
+  static_assert(OP == kProducerLayerNorm, "LayerNorm only");
   static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
   constexpr int RPB = 4 / WPR;                       // rows per workgroup
   __shared__ float red_sum[4];
@@ -154,8 +150,8 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x + (valid ? row : 0) * a.ldx, row_bytes);
 
   uint4 v[CH];
-  uint4 sh[OP == kProducerLayerNorm ? CH : 1];
-  uint4 sc[OP == kProducerLayerNorm ? CH : 1];
+  uint4 sh[CH];
+  uint4 sc[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) v[c] = load16_nt(rx, (uint32_t)(lane + 64 * (part + WPR * c)) * 16u);
   if constexpr (OP == kProducerLayerNorm) {
@@ -177,7 +173,7 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
   // row's amax is taken on the fp32 values: rounding to nearest even is
   // monotone and odd, so max |bf16(y)| = bf16(max |y|).
   float amaxf = 0.0f;
-  if constexpr (OP == kProducerLayerNorm) {
+  {
 #pragma clang fp contract(off)
     float f[CH][8];
 #pragma unroll
@@ -221,19 +217,6 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
         v[c] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-  } else {
-    // chunks past K read zero, and GELU(0) = 0 in both forms
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      float f[8];
-      unpack8(v[c], f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        f[i] = OP == kProducerGelu ? gelu::gelu_erf(f[i]) : gelu::gelu_tanh(f[i]);
-        amaxf = __builtin_fmaxf(amaxf, __builtin_fabsf(f[i]));
-      }
-      v[c] = pack8_bf16(f);
-    }
   }
 
   // per-row quantisation of the bf16 row (the activation quantisation's maths)
@@ -262,9 +245,8 @@ __global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
 }
 
 // z -> bf16(GELU(z)) for every bf16 bit pattern z, erf form then tanh form:
-// read-only data, tabulated on the host at build time with the fp32
-// evaluation of gelu_f32.h (gen_gelu_table.cpp), bit for bit what the
-// per-element kernel computes.
+// read-only data, computed at build time in double precision and rounded
+// once to the nearest bf16 (gen_gelu_table.cpp).
 __device__ __attribute__((aligned(16))) const uint16_t g_gelu_table[2][65536] = {
 #include "gelu_table.inc"
 };
@@ -395,12 +377,10 @@ hipError_t launch_lut(const ProducerArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The table path pays for its per-workgroup 128 KB table copy from about
-// 4 M elements on; 4 waves hold a row of up to 16384 elements, 8 waves a
-// longer one (up to 32768), at most 8 chunks per lane.
-constexpr int64_t kLutMinElements = int64_t(1) << 22;
-constexpr int64_t kLutMaxChunks = 4096;
-
+// Every GELU call takes the table kernel: with the table built in, it
+// measured faster than evaluating GELU per element at every size tried
+// (16 to 1024 rows of 3072 and 12288 elements: 5.8-12.5 against 6.8-16.7 us
+// per call), including one workgroup per four rows below a full chip.
 template <int OP>
 hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
   // waves per row: at 4352 x 12288, 4 ran in 45 us, 8 in 50 us, 16 in
@@ -428,23 +408,20 @@ hipError_t launch_cfg(const ProducerArgs& a, hipStream_t stream) {
 
 template <int OP>
 hipError_t launch_op(const ProducerArgs& a, hipStream_t stream) {
-  const int64_t nchunks = a.K >> 3;
   if constexpr (OP != kProducerLayerNorm) {
-    if (nchunks <= kLutMaxChunks && a.M * a.K >= kLutMinElements) return launch_gelu_lut<OP>(a, stream);
+    return launch_gelu_lut<OP>(a, stream);    // K <= 32768, checked before the launch
+  } else {
+    const int64_t nchunks = a.K >> 3;
+    if (nchunks <= 64) return launch_cfg<OP, 1, 1>(a, stream);
+    if (nchunks <= 128) return launch_cfg<OP, 2, 1>(a, stream);
+    if (nchunks <= 256) return launch_cfg<OP, 2, 2>(a, stream);
+    if (nchunks <= 384) return launch_cfg<OP, 3, 2>(a, stream);
+    if (nchunks <= 512) return launch_cfg<OP, 4, 2>(a, stream);
+    if (nchunks <= 1024) return launch_cfg<OP, 4, 4>(a, stream);
+    if (nchunks <= 1536) return launch_cfg<OP, 6, 4>(a, stream);
+    if (nchunks <= 2048) return launch_cfg<OP, 8, 4>(a, stream);
+    return hipErrorInvalidValue;    // past kProducerMaxK: rejected before the launch
   }
-  if (nchunks <= 64) return launch_cfg<OP, 1, 1>(a, stream);
-  if (nchunks <= 128) return launch_cfg<OP, 2, 1>(a, stream);
-  if (nchunks <= 256) return launch_cfg<OP, 2, 2>(a, stream);
-  if (nchunks <= 384) return launch_cfg<OP, 3, 2>(a, stream);
-  if (nchunks <= 512) return launch_cfg<OP, 4, 2>(a, stream);
-  if (nchunks <= 1024) return launch_cfg<OP, 4, 4>(a, stream);
-  if (nchunks <= 1536) return launch_cfg<OP, 6, 4>(a, stream);
-  if (nchunks <= 2048) return launch_cfg<OP, 8, 4>(a, stream);
-  if constexpr (OP != kProducerLayerNorm) {
-    if (nchunks <= 3072) return launch_cfg<OP, 12, 4>(a, stream);
-    if (nchunks <= 4096) return launch_cfg<OP, 16, 4>(a, stream);
-  }
-  return hipErrorInvalidValue;      // past kProducerMaxK: rejected before the launch
 }
 
 }  // namespace
