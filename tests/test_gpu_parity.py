@@ -286,6 +286,96 @@ def test_extreme_accumulators():
     _linear_case(x, w, None)
 
 
+# the largest K the library accepts: a multiple of 16 with 127^2 K < 2^31
+K_LARGEST = (w8.K_MAX // 16) * 16
+
+
+def _signed_ones(R, K):
+    """Rows of +1.0 (even rows) and -1.0 (odd rows): every code is +-127."""
+    x = np.full((R, K), 0x3F80, np.uint16)
+    x[1::2] = 0xBF80
+    return x
+
+
+@pytest.mark.parametrize("M,N", [(3, 40), (130, 72)])
+def test_linear_largest_k_extreme_accumulators(M, N):
+    """At the largest accepted K, +-127 codes throughout give |acc| =
+    127^2 K, the int32 limit the K bound is set by, with both signs: the
+    GEMM split in K on 64x64 tiles (M = 3) and on 128x128 tiles (M = 130),
+    against the oracle on every output."""
+    x, w = _signed_ones(M, K_LARGEST), _signed_ones(N, K_LARGEST)
+    announce(f"largest K M={M} N={N} K={K_LARGEST} tile={w8.gemm_tile(M, K_LARGEST, N)}")
+    _, exp = _linear_case(x, w, None)
+    assert np.abs(exp["acc"]).max() == 127 * 127 * K_LARGEST < 2**31
+
+
+@pytest.mark.parametrize("M,N", [(4352, 3072), (2048, 4096)])
+def test_linear_largest_k_256_tiles(M, N):
+    """The 256x256-tile kernel at the largest accepted K, whole tiles
+    (4352 x 3072: 204 tiles) and 128-row halves (2048 x 4096: 128 tiles),
+    with +-127 codes throughout. Row m of x and row n of W are +-1.0 by the
+    parity of m and n, so every output is one of four values. Quantisation
+    is per row and per output channel, so the oracle run on rows 0-1 of x
+    and W gives those four values exactly; every element of xq, a_scale,
+    acc and y is compared with them."""
+    K = K_LARGEST
+    assert w8.gemm_tile(M, K, N) == (256, 256)
+    x, w = _signed_ones(M, K), _signed_ones(N, K)
+    wq_e, sw_e = oracle.quantize_weights(w[:2])
+    exp = oracle.linear(x[:2], wq_e, sw_e, None)
+    assert np.abs(exp["acc"]).max() == 127 * 127 * K
+
+    wq, sw = w8.quantize_weights(dev_bf16(w))
+    del w
+    xd = dev_bf16(x)
+    del x
+    ws = torch.empty((w8.workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    acc = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    announce(f"largest K, 256x256 tiles M={M} N={N} K={K}")
+    y = w8.linear(xd, wq, sw, workspace=ws, acc_debug=acc)
+    torch.cuda.synchronize()
+
+    # the codes, on the device (M x K bytes): rows alternate the oracle's two
+    xq_d, sa_d = w8.workspace_views(ws, M, K)
+    for p in (0, 1):
+        assert torch.equal(xq_d[p::2], dev(exp["xq"][p]).expand(M // 2, K)), f"xq rows {p}::2"
+        assert torch.equal(wq[p::2], dev(wq_e[p]).expand(N // 2, K)), f"wq rows {p}::2"
+    assert_equal(host(sa_d), np.tile(exp["s_a"], M // 2), "a_scale")
+    assert_equal(host(sw), np.tile(sw_e, N // 2), "w_scale")
+    assert_equal(host(acc), np.tile(exp["acc"], (M // 2, N // 2)), "acc")
+    assert_bf16_close(host_bits(y), np.tile(exp["y"], (M // 2, N // 2)))
+    del xd, ws, acc, y, wq
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 72, 256), (130, 72, 256), (2048, 4096, 256),
+                                   (4352, 3072, 256)])
+def test_linear_largest_output_stride(M, N, K):
+    """Output rows W8A8_LDO_MAX elements apart, the largest stride accepted
+    (the byte offsets within a 256-row tile stay below 2^32), on the
+    small-M kernel (M = 5), 128x128 tiles (M = 130) and 256x256 tiles as
+    halves (2048 x 4096) and whole (4352 x 3072): every output against the
+    oracle, and the columns beside the output and at the end of every row
+    left as they were."""
+    rng = np.random.default_rng(91 + M)
+    x = random_bf16(rng, (M, K))
+    w = random_bf16(rng, (N, K), 0.02)
+    wq_e, sw_e = oracle.quantize_weights(w)
+    exp = oracle.linear(x, wq_e, sw_e, None)
+    wq, sw = w8.quantize_weights(dev_bf16(w))
+    ldo = w8.LDO_MAX
+    out_full = torch.full((M, ldo), 0x1234, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    announce(f"largest output stride M={M} N={N} K={K} ldo={ldo} "
+             f"path={w8.linear_path(M, K, N)} tile={w8.gemm_tile(M, K, N)}")
+    w8.linear(dev_bf16(x), wq, sw, out=out_full[:, :N])
+    torch.cuda.synchronize()
+    assert_bf16_close(host_bits(out_full[:, :N]), exp["y"])
+    pad = torch.cat([out_full[:, N:N + 256], out_full[:, ldo - 256:]], dim=1)
+    assert (host_bits(pad) == 0x1234).all(), "output padding written"
+    del out_full, pad
+    torch.cuda.empty_cache()
+
+
 def test_linear_subnormal_scales_and_outputs():
     """Weights ~1e-41 (bf16 subnormals) give subnormal fp32 weight scales
     (exact-division quantisation path) and bf16-subnormal outputs, on both
