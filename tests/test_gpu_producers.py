@@ -112,10 +112,12 @@ def _ln_inputs(M, K, G=1, seed=0, outliers=0):
     return x, random_bf16(rng, (G, K), 0.5), random_bf16(rng, (G, K), 0.5)
 
 
-# every launch configuration (1, 2 or 4 waves per row, 1..8 chunks per lane),
-# ragged K and partial last workgroups
+# every launch configuration (1 to 4 waves per row, 1..8 chunks per lane),
+# ragged K and partial last workgroups; rows of 2049-3072 elements take three
+# waves per row up to 1024 rows and two beyond
 LN_SHAPES = [(1, 16), (3, 48), (5, 512), (7, 528), (4, 1024), (9, 1040), (6, 2048), (3, 2064),
-             (10, 3072), (2, 4096), (5, 4112), (3, 8192), (6, 12288), (2, 12304), (3, 16384)]
+             (10, 3072), (1023, 3072), (1024, 2064), (1025, 3072), (2, 4096), (5, 4112),
+             (3, 8192), (6, 12288), (2, 12304), (3, 16384)]
 
 
 @pytest.mark.parametrize("M,K", LN_SHAPES)

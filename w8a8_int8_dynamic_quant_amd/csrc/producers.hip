@@ -12,8 +12,9 @@
 // to even), and, when asked, y itself: what the unfused producer would have
 // written and the quantisation would have read back.
 //
-// The LayerNorm kernel follows the quantisation kernels: one, two or four
-// waves per row (two from K > 1024, four from K > 4096), lane `lane` of wave
+// The LayerNorm kernel follows the quantisation kernels: one to four waves
+// per row (two from K > 1024, or three up to K = 3072 when there are at
+// most 1024 rows; four from K > 4096), lane `lane` of wave
 // part p holding the row's 16-byte chunks lane + 64 (p + WPR c), c < CH, all
 // requested at once (non-temporal: x is read once) and kept in registers
 // through every step, so the row is read from HBM once and written once as
@@ -131,14 +132,18 @@ __device__ __forceinline__ uint32_t row_max_parts(uint32_t v, uint32_t* slot, in
 
 // The modulated LayerNorm fused with the quantisation (OP is always
 // kProducerLayerNorm: GELU takes the table kernel below).
+template <int WPR>
+constexpr int ln_rows_per_block() { return WPR == 3 ? 2 : 4 / WPR; }
+
 template <int OP, int CH, int WPR>
-__global__ __launch_bounds__(256) void producer_quant_kernel(ProducerArgs a) {
+__global__ __launch_bounds__(64 * WPR * ln_rows_per_block<WPR>()) void producer_quant_kernel(
+    ProducerArgs a) {
   static_assert(OP == kProducerLayerNorm, "LayerNorm only");
-  static_assert(WPR == 1 || WPR == 2 || WPR == 4, "waves per row");
-  constexpr int RPB = 4 / WPR;                       // rows per workgroup
-  __shared__ float red_sum[4];
-  __shared__ float red_sq[4];
-  __shared__ uint32_t red_max[4];
+  static_assert(WPR >= 1 && WPR <= 4, "waves per row");
+  constexpr int RPB = ln_rows_per_block<WPR>();      // rows per workgroup
+  __shared__ float red_sum[RPB * WPR];
+  __shared__ float red_sq[RPB * WPR];
+  __shared__ uint32_t red_max[RPB * WPR];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = wave % WPR;
@@ -400,9 +405,9 @@ hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
 
 template <int OP, int CH, int WPR>
 hipError_t launch_cfg(const ProducerArgs& a, hipStream_t stream) {
-  constexpr int RPB = 4 / WPR;
+  constexpr int RPB = ln_rows_per_block<WPR>();
   hipLaunchKernelGGL((producer_quant_kernel<OP, CH, WPR>), dim3((unsigned)((a.M + RPB - 1) / RPB)),
-                     dim3(256), 0, stream, a);
+                     dim3(64 * WPR * RPB), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -415,7 +420,15 @@ hipError_t launch_op(const ProducerArgs& a, hipStream_t stream) {
     if (nchunks <= 64) return launch_cfg<OP, 1, 1>(a, stream);
     if (nchunks <= 128) return launch_cfg<OP, 2, 1>(a, stream);
     if (nchunks <= 256) return launch_cfg<OP, 2, 2>(a, stream);
-    if (nchunks <= 384) return launch_cfg<OP, 3, 2>(a, stream);
+    // rows of 2049-3072 elements: three waves per row (two chunks a lane)
+    // while there are at most 1024 rows, two (three chunks) beyond. Per
+    // call at K = 3072, 16 / 64 / 256 / 1024 rows: 4.5 / 4.5 / 4.8 / 6.4 us
+    // against 5.0 / 5.4 / 5.6 / 6.7; equal at 1536 rows; 2048 / 3072 /
+    // 4352 rows: 8.9 / 11.2 / 15.1 against 8.7 / 10.5 / 13.7 us
+    if (nchunks <= 384) {
+      if (a.M <= 1024) return launch_cfg<OP, 2, 3>(a, stream);
+      return launch_cfg<OP, 3, 2>(a, stream);
+    }
     if (nchunks <= 512) return launch_cfg<OP, 4, 2>(a, stream);
     if (nchunks <= 1024) return launch_cfg<OP, 4, 4>(a, stream);
     if (nchunks <= 1536) return launch_cfg<OP, 6, 4>(a, stream);
