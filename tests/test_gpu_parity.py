@@ -91,6 +91,10 @@ def test_quant_edge_rows():
 
 @pytest.mark.parametrize("M,K,ld", [(1, 16, 16), (3, 48, 64), (5, 1040, 1040), (7, 16400, 16400),
                                     (2, 20000, 20008), (129, 3072, 3080),
+                                    # three and four waves per row, ragged rows and
+                                    # partial last workgroups
+                                    (3, 2064, 2072), (5, 3056, 3056), (2, 3088, 3096),
+                                    (7, 4096, 4104), (1025, 4080, 4080),
                                     # one 256-thread workgroup per row, 4 and 16 chunks per
                                     # thread (rows of 4112-8192 and 24592-32768 elements)
                                     (3, 4112, 4120), (5, 8192, 8192), (2, 24592, 24600),

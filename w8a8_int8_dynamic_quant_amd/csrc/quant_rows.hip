@@ -4,9 +4,10 @@
 // load-time per-output-channel weight quantisation of the W8A8 int8-dynamic
 // linear (Issue 5 probe, "Round two"; Int8 Quantization guide, "Overview").
 //
-// Rows of up to 4096 elements: one or two waves per row (two from 1536
-// elements on, sharing the row's amax through LDS, so each wave's compute
-// after its loads land is half as long). Rows of up to 32768 elements: a
+// Rows of up to 4096 elements: one to four waves per row (two from 1025
+// elements on, three from 2049, four from 3073; rows of 2049-3072 elements
+// take two waves when there are more than 2048 rows), sharing the row's amax
+// through LDS, so each wave's compute after its loads land is short. Rows of up to 32768 elements: a
 // workgroup of 4 waves per row, thread t holding the row's 16-byte chunks t,
 // t+256, ... (8 values each; 4 KiB contiguous per load instruction of the
 // workgroup), the four wave maxima meeting in LDS. Either way every chunk of
@@ -64,22 +65,26 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   if (tid == 0) scale[row] = s;
 }
 
-// Short rows: P waves per row (P = 1 or 2), 4/P rows per workgroup; wave
-// part h of a row holds chunks lane + 64*(c + CHUNKS*h), c < CHUNKS, all
-// requested at once and kept in registers between the amax and the quantise
-// step; all rows are in flight together. With P = 2 the two waves exchange
-// their amax through LDS.
+// Short rows: P waves per row (P = 1 to 4), 4/P rows per workgroup (two
+// for P = 3); wave part h of a row holds chunks lane + 64*(c + CHUNKS*h),
+// c < CHUNKS, all requested at once and kept in registers between the amax
+// and the quantise step; all rows are in flight together. With P > 1 the
+// waves of a row exchange their amax through LDS.
+template <int P>
+constexpr int qw_rows_per_block() { return P == 3 ? 2 : 4 / P; }
+
 template <int CHUNKS, int P, bool F16>
-__global__ __launch_bounds__(256) void quant_rows_wave_kernel(
+__global__ __launch_bounds__(64 * P * qw_rows_per_block<P>()) void quant_rows_wave_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
-  static_assert(P == 1 || P == 2, "one or two waves per row");
-  __shared__ uint32_t part_max[4];
+  static_assert(P >= 1 && P <= 4, "waves per row");
+  constexpr int RPB = qw_rows_per_block<P>();
+  __shared__ uint32_t part_max[RPB * P];
   const int lane = threadIdx.x & 63;
   // wave-uniform row (readfirstlane keeps the row's buffer descriptor scalar)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = wave % P;
-  const int64_t row = (int64_t)blockIdx.x * (4 / P) + wave / P;
+  const int64_t row = (int64_t)blockIdx.x * RPB + wave / P;
   const bool valid = row < R;
   if (P == 1 && !valid) return;
   const uint32_t nchunks = (uint32_t)(K >> 3);
@@ -94,10 +99,13 @@ __global__ __launch_bounds__(256) void quant_rows_wave_kernel(
 #pragma unroll
   for (int c = 0; c < CHUNKS; ++c) amax = absmax_bits8(v[c], amax);
   amax = wave_max_u32(amax);
-  if constexpr (P == 2) {
+  if constexpr (P > 1) {
     if (lane == 0) part_max[wave] = amax;
     lds_barrier();
-    amax = max(part_max[wave & 2], part_max[(wave & 2) + 1]);
+    const int base = wave - part;
+    amax = part_max[base];
+#pragma unroll
+    for (int h = 1; h < P; ++h) amax = max(amax, part_max[base + h]);
     if (!valid) return;
   }
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row * K, (uint32_t)K);
@@ -167,18 +175,26 @@ hipError_t launch_quant_rows_t(const uint16_t* x, int64_t R, int64_t K, int64_t 
   if (R == 0) return hipSuccess;
   const int64_t nchunks = K >> 3;
   const int64_t per_lane = (nchunks + 63) / 64;
-  if (per_lane <= 8) {                    // K <= 4096: one or two waves per row
-    const dim3 block(256);
+  if (per_lane <= 8) {                    // K <= 4096: one to four waves per row
 #define W8A8_QW(C, P)                                                                   \
     hipLaunchKernelGGL((quant_rows_wave_kernel<C, P, F16>),                             \
-                       dim3((unsigned)((R + 4 / P - 1) / (4 / P))), block, 0, stream, x, R, \
-                       K, ldx, q, scale);                                               \
+                       dim3((unsigned)((R + qw_rows_per_block<P>() - 1) / qw_rows_per_block<P>())), \
+                       dim3(64 * P * qw_rows_per_block<P>()), 0, stream, x, R, K, ldx, q, scale); \
     return hipGetLastError();
+    // three and four waves per row with two chunks a lane, rather than two
+    // waves with three or four: per call, same bits, 64 / 512 / 1024 / 4352
+    // rows of 4096 elements 3.6 / 4.2 / 5.2 / 11.5 us against 5.1 / 5.6 /
+    // 6.5 / 12.4; of 3072 elements, 64 / 512 / 1024 / 2048 rows 3.6 / 4.0 /
+    // 5.0 / 6.3 against 4.1 / 4.7 / 5.4 / 6.9, while 4352 rows measured the
+    // same either way (10.0-10.3 us), so more rows than 2048 keep two waves
     if (per_lane <= 1) { W8A8_QW(1, 1) }
     if (per_lane <= 2) { W8A8_QW(2, 1) }
     if (per_lane <= 4) { W8A8_QW(2, 2) }
-    if (per_lane <= 6) { W8A8_QW(3, 2) }
-    W8A8_QW(4, 2)
+    if (per_lane <= 6) {
+      if (R <= 2048) { W8A8_QW(2, 3) }
+      W8A8_QW(3, 2)
+    }
+    W8A8_QW(2, 4)
 #undef W8A8_QW
   }
   const int64_t per_thread = (nchunks + 255) / 256;
