@@ -65,7 +65,8 @@ def test_f16_quant_exhaustive_sweep():
 
 
 @pytest.mark.parametrize("R,K,ld", [(1, 16, 16), (3, 48, 64), (5, 1040, 1040), (7, 3072, 3080),
-                                    (3, 2064, 2072), (5, 3088, 3096),
+                                    (3, 2064, 2072), (5, 3088, 3096), (3, 14000, 14000),
+                                    (2049, 4112, 4120),
                                     (9, 4096, 4096), (4, 12288, 12288), (3, 16400, 16408),
                                     (2, 40000, 40000), (3, 4112, 4120), (2, 8192, 8192),
                                     (2, 24592, 24600), (3, 32768, 32768)])

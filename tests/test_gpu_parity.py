@@ -95,10 +95,12 @@ def test_quant_edge_rows():
                                     # partial last workgroups
                                     (3, 2064, 2072), (5, 3056, 3056), (2, 3088, 3096),
                                     (7, 4096, 4104), (1025, 4080, 4080),
-                                    # one 256-thread workgroup per row, 4 and 16 chunks per
-                                    # thread (rows of 4112-8192 and 24592-32768 elements)
-                                    (3, 4112, 4120), (5, 8192, 8192), (2, 24592, 24600),
-                                    (3, 32768, 32768)])
+                                    # one workgroup of eight waves per row, 2 to 8 chunks
+                                    # per thread, and four waves (4 chunks) for rows of
+                                    # 4112-8192 elements beyond 2048 rows
+                                    (3, 4112, 4120), (5, 8192, 8192), (3, 14000, 14000),
+                                    (2, 24592, 24600), (3, 32768, 32768), (2049, 4112, 4120),
+                                    (2050, 8192, 8192)])
 def test_quant_ragged_and_strided(M, K, ld):
     rng = np.random.default_rng(M * 7 + K)
     full = random_bf16(rng, (M, ld))

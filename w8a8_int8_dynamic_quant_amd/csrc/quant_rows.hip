@@ -7,10 +7,12 @@
 // Rows of up to 4096 elements: one to four waves per row (two from 1025
 // elements on, three from 2049, four from 3073; rows of 2049-3072 elements
 // take two waves when there are more than 2048 rows), sharing the row's amax
-// through LDS, so each wave's compute after its loads land is short. Rows of up to 32768 elements: a
-// workgroup of 4 waves per row, thread t holding the row's 16-byte chunks t,
-// t+256, ... (8 values each; 4 KiB contiguous per load instruction of the
-// workgroup), the four wave maxima meeting in LDS. Either way every chunk of
+// through LDS, so each wave's compute after its loads land is short. Rows
+// of up to 32768 elements: a workgroup of NW = 8 waves per row (4 for rows
+// of up to 8192 elements when there are more than 2048 rows), thread t
+// holding the row's 16-byte chunks t, t + 64 NW, ... (8 values each; 64 NW
+// x 16 bytes contiguous per load instruction of the workgroup), the wave
+// maxima meeting in LDS. Either way every chunk of
 // a row is requested at once and the whole matrix is launched at once (a
 // persistent grid walking rows with the next row prefetched measured slower:
 // 34.3 against 29.8 us for 4352 x 12288). Loads go through a buffer
@@ -32,11 +34,11 @@ __device__ __forceinline__ void store8(uint2 q, __amdgpu_buffer_rsrc_t r, uint32
   __builtin_amdgcn_raw_buffer_store_b64((v2u){q.x, q.y}, r, off, 0, 0);
 }
 
-template <int CHT, bool F16>
-__global__ __launch_bounds__(256) void quant_rows_kernel(
+template <int CHT, int NW, bool F16>
+__global__ __launch_bounds__(64 * NW) void quant_rows_kernel(
     const uint16_t* __restrict__ x, int64_t R, int64_t K, int64_t ldx,
     int8_t* __restrict__ q, float* __restrict__ scale) {
-  __shared__ uint32_t wmax[4];             // per-wave amax
+  __shared__ uint32_t wmax[NW];            // per-wave amax
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t nchunks = (uint32_t)(K >> 3);
@@ -44,14 +46,16 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + row * ldx, (uint32_t)K * 2u);
   uint4 v[CHT];
 #pragma unroll
-  for (int u = 0; u < CHT; ++u) v[u] = load16_nt(rx, (uint32_t)(tid + 256 * u) * 16u);
+  for (int u = 0; u < CHT; ++u) v[u] = load16_nt(rx, (uint32_t)(tid + 64 * NW * u) * 16u);
   uint32_t amax = 0;
 #pragma unroll
   for (int u = 0; u < CHT; ++u) amax = absmax_bits8(v[u], amax);
   amax = wave_max_u32(amax);
   if ((tid & 63) == 0) wmax[wave] = amax;
   lds_barrier();
-  amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  amax = wmax[0];
+#pragma unroll
+  for (int h = 1; h < NW; ++h) amax = max(amax, wmax[h]);
   const float s = row_scale<F16>(amax);
   const bool zero = (amax == 0);
   const bool exact_div = (__float_as_uint(s) & 0x7f800000u) == 0;  // subnormal s
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + row * K, (uint32_t)K);
 #pragma unroll
   for (int u = 0; u < CHT; ++u) {
-    const uint32_t idx = (uint32_t)(tid + 256 * u);
+    const uint32_t idx = (uint32_t)(tid + 64 * NW * u);
     store8(quant8<F16>(v[u], s, r, zero, exact_div), rq, idx < nchunks ? idx * 8u : kOOB);
   }
   if (tid == 0) scale[row] = s;
@@ -161,11 +165,11 @@ __global__ __launch_bounds__(256) void quant_rows_long_kernel(
   if (lane == 0) scale[row] = s;
 }
 
-template <int C, bool F16>
+template <int C, int NW, bool F16>
 hipError_t launch_cht(const uint16_t* x, int64_t R, int64_t K, int64_t ldx, int8_t* q, float* scale,
                       hipStream_t stream) {
-  hipLaunchKernelGGL((quant_rows_kernel<C, F16>), dim3((unsigned)R), dim3(256), 0, stream, x, R, K,
-                     ldx, q, scale);
+  hipLaunchKernelGGL((quant_rows_kernel<C, NW, F16>), dim3((unsigned)R), dim3(64 * NW), 0, stream, x,
+                     R, K, ldx, q, scale);
   return hipGetLastError();
 }
 
@@ -197,12 +201,19 @@ hipError_t launch_quant_rows_t(const uint16_t* x, int64_t R, int64_t K, int64_t 
     W8A8_QW(2, 4)
 #undef W8A8_QW
   }
-  const int64_t per_thread = (nchunks + 255) / 256;
-  if (per_thread <= 4) return launch_cht<4, F16>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 6) return launch_cht<6, F16>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 8) return launch_cht<8, F16>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 12) return launch_cht<12, F16>(x, R, K, ldx, q, scale, stream);
-  if (per_thread <= 16) return launch_cht<16, F16>(x, R, K, ldx, q, scale, stream);
+  // eight waves per row rather than four (half the chunks a thread): per
+  // call, same bits, 64 / 1024 / 4352 rows of 12288 elements 4.5 / 9.7 /
+  // 26.9 us against 5.9 / 11.0 / 27.8; of 24576 elements 7.7 / 16.2 /
+  // 52.1 against 11.2 / 19.4 / 54.4; of 8192 elements 4.2 / 7.4 against
+  // 4.8 / 8.3 at 64 / 1024 rows, but 19.7 against 19.3 at 4352 rows, so
+  // rows of up to 8192 elements keep four waves beyond 2048 rows
+  const int64_t per8 = (nchunks + 511) / 512;     // chunks per thread of eight waves
+  if (per8 <= 2 && R > 2048) return launch_cht<4, 4, F16>(x, R, K, ldx, q, scale, stream);
+  if (per8 <= 2) return launch_cht<2, 8, F16>(x, R, K, ldx, q, scale, stream);
+  if (per8 <= 3) return launch_cht<3, 8, F16>(x, R, K, ldx, q, scale, stream);
+  if (per8 <= 4) return launch_cht<4, 8, F16>(x, R, K, ldx, q, scale, stream);
+  if (per8 <= 6) return launch_cht<6, 8, F16>(x, R, K, ldx, q, scale, stream);
+  if (per8 <= 8) return launch_cht<8, 8, F16>(x, R, K, ldx, q, scale, stream);
   hipLaunchKernelGGL(quant_rows_long_kernel<F16>, dim3((unsigned)((R + 3) / 4)), dim3(256), 0,
                      stream, x, R, K, ldx, q, scale);
   return hipGetLastError();
