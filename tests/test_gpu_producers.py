@@ -274,12 +274,17 @@ def test_gelu_every_bf16_value_is_the_table_entry(host_tables, form, approximate
 @pytest.mark.parametrize("approximate", ["none", "tanh"])
 @pytest.mark.parametrize("M,K", [(1100, 4112), (262160, 16), (400, 12288), (3001, 1552),
                                  (520, 8192), (300, 16384), (260, 16400), (180, 24576),
-                                 (130, 32768), (600, 24576)])
+                                 (130, 32768), (600, 24576),
+                                 # sixteen waves per row (at most 512 rows of at most
+                                 # 16384 elements), over one and two sweeps of the grid,
+                                 # and four waves just past 512 rows
+                                 (512, 3088), (340, 12304), (512, 16384), (513, 3072)])
 def test_gelu_table_path_shapes(approximate, M, K):
     """Ragged K (past-K chunks in a lane's last slots), one to eight chunks
-    per lane on four waves per row up to K = 16384 and on eight waves per row
-    beyond it (K = 16400, 24576, 32768), and more rows than the grid takes
-    in one pass (on both: 1100 x 4112, 600 x 24576)."""
+    per lane on four waves per row up to K = 16384 (more than 512 rows),
+    sixteen waves per row (at most 512 rows), eight waves per row beyond
+    K = 16384 (K = 16400, 24576, 32768), and more rows than the grid takes
+    in one pass (1100 x 4112, 600 x 24576, 340 x 12304, 512 x 16384)."""
     rng = np.random.default_rng(M + K)
     st = run_gelu(random_bf16(rng, (M, K), 1.5), approximate)
     assert st["n_not_nearest"] <= max(2, st["n"] // 1000), st

@@ -38,8 +38,9 @@
 // carries it as read-only data; nothing is computed or written for it at run
 // time. The kernel copies it into LDS once per workgroup (one 1024-thread
 // workgroup per compute unit, four rows at a time with four waves to a row,
-// or two rows with eight waves for rows of more than 16384 elements), and
-// each element is one LDS lookup.
+// two rows with eight waves for rows of more than 16384 elements, or one
+// row with all sixteen waves when there are at most 512 rows of up to 16384
+// elements), and each element is one LDS lookup.
 #include "producers.h"
 #include "row_groups.h"
 #include "w8a8_device.h"
@@ -391,6 +392,17 @@ hipError_t launch_gelu_lut(const ProducerArgs& a, hipStream_t stream) {
   // waves per row: at 4352 x 12288, 4 ran in 45 us, 8 in 50 us, 16 in
   // 57 us (wider rows mean more waves at each barrier); rows of more than
   // 16384 elements take 8, so that a lane holds at most 8 chunks
+  // up to 512 rows of up to 16384 elements: sixteen waves per row (one
+  // row per workgroup iteration), so that few rows still spread over many
+  // waves; per call, erf form, 16 / 64 / 256 / 512 rows of 12288 elements
+  // 5.7 / 5.9 / 7.3 / 9.6 us against 9.2 / 9.8 / 11.7 / 12.6 with four, of
+  // 3072 elements 4.4 / 4.5 / 4.7 / 5.9 against 5.4 / 6.0 / 6.0 / 6.3; at
+  // 1024 rows equal (12288) or slower (3072: 8.7 against 6.6 us)
+  if (a.M <= 512) {
+    const int64_t p16 = ((a.K >> 3) + 1023) / 1024;
+    if (p16 <= 1) return launch_lut<OP, 1, 16>(a, stream);
+    if (p16 <= 2) return launch_lut<OP, 2, 16>(a, stream);
+  }
   constexpr int W = 4;
   const int64_t per_lane = ((a.K >> 3) + 64 * W - 1) / (64 * W);
   if (per_lane <= 1) return launch_lut<OP, 1, W>(a, stream);
